@@ -1,0 +1,285 @@
+// Internal layout definitions and device codecs of the HIP path.
+//
+// Element formats follow the OCP Microscaling Formats (MX) v1.0 definitions
+// (E2M1, E4M3 "FN", E8M0). NVFP4 = E2M1 elements with an E4M3 scale per 16
+// elements and an FP32 global scale g = amax / (6 * 448); MXFP8 = E4M3
+// elements with an E8M0 scale per 32 elements (MegaMoE post, "Our approach":
+// block-16 and block-32 scaling).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_fp4.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kTileK = 128;         // K extent of one weight micro-tile
+constexpr int kStrip = 16;          // N rows of one weight micro-tile
+constexpr int kNvTileBytes = 1024;  // NVFP4 codes of a 16 x 128 micro-tile
+constexpr int kNvTileScale = 128;   // its 16 x 8 E4M3 scales
+constexpr int kF8TileBytes = 2048;  // MXFP8 codes of a 16 x 128 micro-tile
+constexpr int kF8TileScale = 64;    // its 16 x 4 E8M0 scales
+constexpr int kPermChunk = 1024;    // routes per block in the permutation kernels
+constexpr int kNumBM = 4;           // M-tile sizes with a device tile list
+__host__ __device__ constexpr int bm_of(int i) { return 16 << i; }  // 16, 32, 64, 128
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 64;
+constexpr uint32_t kBlobMagic0 = 0x5746454Du;  // "MEFW"
+constexpr uint32_t kBlobMagic1 = 0x34504634u;  // "4FP4"
+constexpr uint32_t kBlobVersion = 1;
+constexpr size_t kBlobHeader = 4096;
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Prepared weight blob
+// ---------------------------------------------------------------------------
+// [header 4096 B][g1: E f32][g2: E f32][amax scratch: 2E u32]
+// [W1 codes][W1 scales][W2 codes][W2 scales]
+// Each weight matrix W[N][K] (N1 x H for W1, H x I for W2) is cut into
+// micro-tiles of 16 rows x 128 k stored tile-row-major: tile (nt, kt) at
+// (nt * K/128 + kt) * tile_bytes. Inside a tile the bytes are the exact
+// register image a 64-lane wave feeds to the matrix cores:
+//  NVFP4 (16x16x32 bf16/f16 MFMA after dequantization): lane l owns 16 bytes at
+//    l*16; row n = l % 16; dword j (0..3) holds the 8 codes
+//    k = 32 j + 8 (l / 16) + [0, 8), element i in nibble i (low nibble first).
+//    Scales: 32 dwords; dword (l >> 5) * 16 + (l & 15) holds, in byte j, the
+//    E4M3 scale of row l % 16 for 16-block 2 j + (l >> 5) of the tile.
+//  MXFP8 (16x16x128 scaled f8f6f4 MFMA): lane l owns 32 bytes at l*32; row
+//    n = l % 16, q = l / 16; byte b < 16 is k = 16 q + b, byte b >= 16 is
+//    k = 64 + 16 q + (b - 16). Scales: byte l is the E8M0 scale of row l % 16
+//    for 32-block l / 16 of the tile.
+// SwiGLU W1 rows are interleaved by strips of 16: prepared strip 2s holds gate
+// rows [16 s, 16 s + 16) and strip 2s + 1 the up rows I + [16 s, 16 s + 16), so
+// one wave sees matching gate/up accumulators in the same lanes.
+struct BlobHeader {
+    uint32_t magic0, magic1, version, wfmt;
+    int32_t E, H, I, N1, act, pad0;
+    uint64_t off_g1, off_g2, off_amax, off_w1, off_s1, off_w2, off_s2, total;
+};
+
+struct BlobLayout {
+    BlobHeader h;
+    size_t w_tile_bytes, s_tile_bytes;
+};
+
+inline bool make_blob_layout(const moe_dims& d, BlobLayout* L) {
+    BlobHeader& h = L->h;
+    h.magic0 = kBlobMagic0;
+    h.magic1 = kBlobMagic1;
+    h.version = kBlobVersion;
+    h.wfmt = (uint32_t)d.wfmt;
+    h.E = d.E;
+    h.H = d.H;
+    h.I = d.I;
+    h.N1 = d.act == MOE_ACT_SWIGLU ? 2 * d.I : d.I;
+    h.act = d.act;
+    h.pad0 = 0;
+    const bool nv = d.wfmt == MOE_FMT_NVFP4;
+    L->w_tile_bytes = nv ? kNvTileBytes : kF8TileBytes;
+    L->s_tile_bytes = nv ? kNvTileScale : kF8TileScale;
+    const size_t E = (size_t)d.E;
+    const size_t t1 = (size_t)(h.N1 / kStrip) * (size_t)(d.H / kTileK);  // tiles per expert
+    const size_t t2 = (size_t)(d.H / kStrip) * (size_t)(d.I / kTileK);
+    size_t off = kBlobHeader;
+    h.off_g1 = off; off = align256(off + E * 4);
+    h.off_g2 = off; off = align256(off + E * 4);
+    h.off_amax = off; off = align256(off + 2 * E * 4);
+    h.off_w1 = off; off = align256(off + E * t1 * L->w_tile_bytes);
+    h.off_s1 = off; off = align256(off + E * t1 * L->s_tile_bytes);
+    h.off_w2 = off; off = align256(off + E * t2 * L->w_tile_bytes);
+    h.off_s2 = off; off = align256(off + E * t2 * L->s_tile_bytes);
+    h.total = off;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace
+// ---------------------------------------------------------------------------
+enum WsView {
+    V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,
+    V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
+    V_NUM_PUBLIC,
+    V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_YACC, V_NUM
+};
+
+struct WsPlan {
+    size_t off[V_NUM];
+    size_t bytes[V_NUM];
+    size_t total;
+    int nblk;  // permutation blocks
+};
+
+inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p) {
+    const size_t R = (size_t)T * K, E = (size_t)d.E, H = (size_t)d.H, I = (size_t)d.I;
+    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN;
+    const bool f8 = mode == MOE_MXFP8;
+    p->nblk = (int)((R + kPermChunk - 1) / kPermChunk);
+    for (int v = 0; v < V_NUM; ++v) p->bytes[v] = 0;
+    p->bytes[V_IDS] = R * 4;
+    p->bytes[V_TOPW] = R * 4;
+    p->bytes[V_COUNTS] = E * 4;
+    p->bytes[V_OFFSETS] = (E + 1) * 4;
+    p->bytes[V_R2R] = R * 4;
+    p->bytes[V_RT2ROW] = R * 4;
+    p->bytes[V_TILES] = (size_t)kNumBM * (E + 1) * 4;
+    p->bytes[V_BHIST] = (size_t)p->nblk * E * 4 * 2;
+    p->bytes[V_MISC] = 256;
+    if (nv4) {
+        p->bytes[V_XCODES] = (size_t)T * H / 2;
+        p->bytes[V_XSCALES] = (size_t)T * H / 16;
+        p->bytes[V_XG] = (size_t)T * 4;
+        p->bytes[V_XDEQ] = (size_t)T * H * 2;
+        p->bytes[V_A2F] = R * I * 4;
+        p->bytes[V_A2CODES] = R * I / 2;
+        p->bytes[V_A2SCALES] = R * I / 16;
+        p->bytes[V_A2G] = R * 4;
+        p->bytes[V_A2DEQ] = R * I * 2;
+    } else if (f8) {
+        p->bytes[V_XCODES] = (size_t)T * H;
+        p->bytes[V_XSCALES] = (size_t)T * H / 32;
+        p->bytes[V_A2F] = R * I * 4;
+        p->bytes[V_A2CODES] = R * I;
+        p->bytes[V_A2SCALES] = R * I / 32;
+    } else {
+        p->bytes[V_A2F] = R * I * 2;  // bf16 FC2 input
+    }
+    p->bytes[V_O] = R * H * 4;
+    p->bytes[V_YACC] = (size_t)T * H * 4;
+    size_t off = 0;
+    for (int v = 0; v < V_NUM; ++v) {
+        p->off[v] = off;
+        off = align256(off + p->bytes[v]);
+    }
+    p->total = off;
+}
+
+// misc region (u32 words): [0] x amax bits, [1] FC2-input amax bits
+constexpr int kMiscXAmax = 0, kMiscA2Amax = 1;
+
+// ---------------------------------------------------------------------------
+// Device codecs (written independently of any reference implementation)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+// E2M1 round-to-nearest-even with saturation, as thresholds on |u|: the
+// midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 go to the neighbour whose
+// mantissa bit is 0. Returns the 4-bit code with the sign of u.
+__device__ __forceinline__ uint32_t e2m1_code(float u) {
+    const float a = fabsf(u);
+    uint32_t m;
+    if (a <= 0.25f) m = 0;
+    else if (a < 0.75f) m = 1;
+    else if (a <= 1.25f) m = 2;
+    else if (a < 1.75f) m = 3;
+    else if (a <= 2.5f) m = 4;
+    else if (a < 3.5f) m = 5;
+    else if (a <= 5.0f) m = 6;
+    else m = 7;
+    return m | ((f2u(u) >> 28) & 8u);
+}
+
+// E4M3 "FN" round-to-nearest-even, saturating to +-448, from the fp32 bits.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+    const uint32_t s = (f2u(x) >> 24) & 0x80u;
+    const float a = fabsf(x);
+    if (!(a < 448.0f)) return s | 0x7Eu;
+    if (a < 0.015625f) {                      // below 2^-6: subnormal grid m * 2^-9
+        const float q = a * 512.0f;           // exact
+        return s | (uint32_t)__builtin_rintf(q);  // 0..8; 8 is the first normal (0x08)
+    }
+    const uint32_t u = f2u(a);
+    int e = (int)((u >> 23) & 0xFF) - 127;     // -6 .. 8
+    uint32_t keep = (u >> 20) & 7u;
+    const uint32_t rem = u & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+    if (keep == 8u) { keep = 0; ++e; }
+    uint32_t c = ((uint32_t)(e + 7) << 3) | keep;
+    if (c > 0x7Eu) c = 0x7Eu;
+    return s | c;
+}
+
+// Value of a non-NaN E4M3 code.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    const uint32_t ef = (c >> 3) & 15u, m = c & 7u;
+    float v = ef ? u2f(((ef + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -v : v;
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The 8 E2M1 values of one 32-bit word (element i in nibble i) as fp32, by the
+// hardware converter at unit scale (exact for every code).
+__device__ __forceinline__ void e2m1x8_to_f32(uint32_t w, float* out) {
+    const f32x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    out[0] = c0[0]; out[1] = c0[1]; out[2] = c1[0]; out[3] = c1[1];
+    out[4] = c2[0]; out[5] = c2[1]; out[6] = c3[0]; out[7] = c3[1];
+}
+
+// floor(log2(a)) for a finite a > 0, exactly, from the fp32 bits.
+__device__ __forceinline__ int floor_log2(float a) {
+    const uint32_t u = f2u(a);
+    const int e = (int)((u >> 23) & 0xFF);
+    if (e) return e - 127;
+    return (31 - __builtin_clz(u & 0x7FFFFFu)) - 149;
+}
+
+// bf16 round-to-nearest-even of a finite fp32.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    uint32_t u = f2u(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// NVFP4 quantization of one 16-element block with global scale g:
+//   s = a_b / (6 g), sf = E4M3(s), d = float(sf) * g, code_i = E2M1(v_i / d);
+// every operation is one IEEE fp32 operation in this order. g == 0 or d == 0
+// leaves only the sign bit of each code. Writes 8 packed bytes (even element in
+// the low nibble) to `codes`, the scale byte, and returns the codes' block as
+// two u32 for callers that dequantize.
+__device__ __forceinline__ void nvfp4_block(const float* v, float g, uint32_t* packed /*[2]*/,
+                                            uint32_t* sf_out) {
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    uint32_t sf = 0;
+    float d = 0.0f;
+    if (g != 0.0f) {
+        const float six_g = __fmul_rn(6.0f, g);
+        sf = e4m3_code(__fdiv_rn(ab, six_g));
+        d = __fmul_rn(e4m3_value(sf), g);
+    }
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t c = (d != 0.0f) ? e2m1_code(__fdiv_rn(v[i], d)) : ((f2u(v[i]) >> 28) & 8u);
+        if (i < 8) w0 |= c << (4 * i); else w1 |= c << (4 * (i - 8));
+    }
+    packed[0] = w0;
+    packed[1] = w1;
+    *sf_out = sf;
+}
+
+// MXFP8 quantization of one 32-element block (OCP MX v1.0 scale rule):
+// X = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an all-zero
+// block), elements E4M3(v * 2^-X). Returns the E8M0 code.
+__device__ __forceinline__ uint32_t mxfp8_block(const float* v, uint8_t* codes /*[32]*/) {
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    int X = ab == 0.0f ? -127 : floor_log2(ab) - 8;
+    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+    const float inv = u2f((uint32_t)(127 - X) << 23);  // 2^-X, X <= 119 for finite input
+#pragma unroll
+    for (int i = 0; i < 32; ++i) codes[i] = (uint8_t)e4m3_code(__fmul_rn(v[i], inv));
+    return (uint32_t)(X + 127);
+}
+
+}  // namespace moe

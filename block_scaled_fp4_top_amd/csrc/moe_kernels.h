@@ -1,0 +1,73 @@
+// Host-side launchers of the HIP kernels (each defined in the .hip file that
+// holds its kernels). All launches are asynchronous on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
+                        uint32_t* misc, hipStream_t s);
+hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* bhist,
+                          int32_t* bbase, int32_t* counts, int32_t* offsets, int32_t* tiles,
+                          int32_t* r2r, int32_t* rt2row, hipStream_t s);
+
+// Row quantizers. kind: 0 NVFP4 one global scale (from the amax in *amax_slot),
+// 1 NVFP4 one global scale per row, 2 MXFP8. in_bf16: input rows are bf16
+// (else fp32). deq (NVFP4 only, may be null): fp16 [rows][cols] of code * sf.
+enum QuantKind { QK_NV_TENSOR = 0, QK_NV_ROW = 1, QK_MX = 2 };
+hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* amax_slot, hipStream_t s);
+hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
+                             const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
+                             uint16_t* deq, hipStream_t s);
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, hipStream_t s);
+hipError_t launch_finalize(const void* O, int is_bf16, const int32_t* rt2row, const float* w,
+                           int T, int K, int H, uint16_t* y, hipStream_t s);
+
+// Weight preparation (one matrix family W[E][N][K] at a time).
+hipError_t launch_prep_amax(const float* w, int E, size_t per_expert, uint32_t* amax, hipStream_t s);
+hipError_t launch_prep_nvfp4(const float* w, int E, int N, int K, int swiglu_I,
+                             const uint32_t* amax, float* g, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s);
+hipError_t launch_prep_mxfp8(const float* w, int E, int N, int K, int swiglu_I, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s);
+
+// Grouped GEMMs.
+enum GemmAB { AB_F16_NV = 0, AB_BF16_NV = 1, AB_FP8 = 2 };
+enum GemmEpi { EPI_FC1 = 0, EPI_FC2 = 1 };
+
+struct GemmArgs {
+    // A: activations. gather != 0: A row of permuted row r is row_to_route[r] / topk.
+    const void* a;
+    const uint8_t* a_scales;  // MXFP8 E8M0 [rows][Kdim/32]
+    const float* a_g;         // NVFP4 activation global scale(s), null for W4A16
+    int a_g_per_row;
+    int gather;
+    const int32_t* row_to_route;
+    int topk;
+    // B: prepared weights of this GEMM
+    const uint8_t* b_codes;
+    const uint8_t* b_scales;
+    const float* b_g;  // per-expert NVFP4 global scale, null for MXFP8
+    int N, Kdim;
+    // tile list
+    const int32_t* offsets;
+    const int32_t* tiles;  // [E+1] for this BM
+    int E;
+    int mt_max;
+    // epilogue
+    int act, on_input, I;
+    const float* topw;
+    float* out_f32;      // FC1: fp32 [R][I] (quantized modes); FC2: O [R][N]
+    uint16_t* out_bf16;  // FC1 W4A16: bf16 [R][I]
+    uint32_t* amax_slot; // FC1: amax of the FC2 input (quantized modes)
+    float* yacc;         // FC2 fused: [T][N]
+    int fused;
+};
+
+hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,369 @@
+// Block quantizers (S3 FC1 input, S5 FC2 input, S0 weights), the finalize
+// (S7) and small helper kernels.
+#include "moe_internal.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float wave_max(float m) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    return m;
+}
+
+// 16 consecutive values starting at element `idx` of a bf16 or fp32 row.
+template <bool BF16>
+__device__ __forceinline__ void load16(const void* base, size_t idx, float* v) {
+    if (BF16) {
+        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        const uint4 q0 = p[0], q1 = p[1];
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = u2f(w[i] << 16);
+            v[2 * i + 1] = u2f(w[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 q = p[i];
+            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+    if (BF16) return u2f((uint32_t)static_cast<const uint16_t*>(base)[idx] << 16);
+    return static_cast<const float*>(base)[idx];
+}
+
+// fp16 values code * sf of one NVFP4 block (exact: at most 6 significant bits
+// in [2^-10, 2688]) into 8 dwords.
+__device__ __forceinline__ void nvfp4_deq_f16(const uint32_t* packed, uint32_t sf, uint32_t* out) {
+    const float s = e4m3_value(sf);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        float c[8];
+        e2m1x8_to_f32(packed[w], c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[w * 4 + i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(c[2 * i] * s, c[2 * i + 1] * s));
+    }
+}
+
+// One wave per row, 4 rows per block.
+template <int KIND, bool BF16>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ v, int rows,
+                                                         int cols,
+                                                         const uint32_t* __restrict__ amax_slot,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales,
+                                                         float* __restrict__ g,
+                                                         uint16_t* __restrict__ deq) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const size_t base = (size_t)row * cols;
+    if (KIND == QK_MX) {
+        const int nb = cols / 32;
+        for (int b = lane; b < nb; b += 64) {
+            float vv[32];
+            load16<BF16>(v, base + (size_t)b * 32, vv);
+            load16<BF16>(v, base + (size_t)b * 32 + 16, vv + 16);
+            uint8_t c[32];
+            const uint32_t e8 = mxfp8_block(vv, c);
+            uint4* dst = reinterpret_cast<uint4*>(codes + base + (size_t)b * 32);
+            dst[0] = *reinterpret_cast<const uint4*>(c);
+            dst[1] = *reinterpret_cast<const uint4*>(c + 16);
+            scales[(size_t)row * nb + b] = (uint8_t)e8;
+        }
+        return;
+    }
+    float gg;
+    if (KIND == QK_NV_TENSOR) {
+        gg = __fdiv_rn(u2f(*amax_slot), 2688.0f);
+        if (row == 0 && lane == 0) g[0] = gg;
+    } else {
+        float m = 0.0f;
+        for (int i = lane; i < cols; i += 64) m = fmaxf(m, fabsf(load1<BF16>(v, base + i)));
+        m = wave_max(m);
+        gg = __fdiv_rn(m, 2688.0f);
+        if (lane == 0) g[row] = gg;
+    }
+    const int nb = cols / 16;
+    for (int b = lane; b < nb; b += 64) {
+        float vv[16];
+        load16<BF16>(v, base + (size_t)b * 16, vv);
+        uint32_t packed[2], sf;
+        nvfp4_block(vv, gg, packed, &sf);
+        *reinterpret_cast<uint2*>(codes + base / 2 + (size_t)b * 8) = make_uint2(packed[0], packed[1]);
+        scales[(size_t)row * nb + b] = (uint8_t)sf;
+        if (deq) {
+            uint32_t h[8];
+            nvfp4_deq_f16(packed, sf, h);
+            uint4* dst = reinterpret_cast<uint4*>(deq + base + (size_t)b * 16);
+            dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+            dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        }
+    }
+}
+
+// Max |v| over n elements into *slot (as fp32 bits; order-free atomicMax on
+// non-negative floats compared as unsigned integers).
+template <bool BF16>
+__global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ v, size_t n,
+                                                   uint32_t* __restrict__ slot) {
+    float m = 0.0f;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        m = fmaxf(m, fabsf(load1<BF16>(v, i)));
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        atomicMax(slot, f2u(m));
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        p[i] = v;
+}
+
+__global__ void yacc_to_bf16_kernel(const float* __restrict__ yacc, size_t n,
+                                    uint16_t* __restrict__ y) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        y[i] = bf16_rne(yacc[i]);
+}
+
+// Deterministic finalize: one block per token; the token's K route rows and
+// weights are staged in LDS, each thread reduces 4 columns over k = 0..K-1 in
+// order in fp32 and rounds once to bf16.
+template <bool BF16>
+__global__ __launch_bounds__(256) void finalize_kernel(const void* __restrict__ O,
+                                                       const int32_t* __restrict__ rt2row,
+                                                       const float* __restrict__ w, int K, int H,
+                                                       uint16_t* __restrict__ y) {
+    __shared__ int32_t s_row[kMaxK];
+    __shared__ float s_w[kMaxK];
+    const int t = blockIdx.x;
+    if (threadIdx.x < K) {
+        s_row[threadIdx.x] = rt2row[(size_t)t * K + threadIdx.x];
+        s_w[threadIdx.x] = w ? w[(size_t)t * K + threadIdx.x] : 1.0f;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x * 4; c < H; c += 1024) {
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        for (int k = 0; k < K; ++k) {
+            const size_t off = (size_t)s_row[k] * H + c;
+            float o0, o1, o2, o3;
+            if (BF16) {
+                const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(O) + off);
+                o0 = u2f(q.x << 16); o1 = u2f(q.x & 0xFFFF0000u);
+                o2 = u2f(q.y << 16); o3 = u2f(q.y & 0xFFFF0000u);
+            } else {
+                const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + off);
+                o0 = q.x; o1 = q.y; o2 = q.z; o3 = q.w;
+            }
+            const float wk = s_w[k];
+            a0 = __fmaf_rn(wk, o0, a0); a1 = __fmaf_rn(wk, o1, a1);
+            a2 = __fmaf_rn(wk, o2, a2); a3 = __fmaf_rn(wk, o3, a3);
+        }
+        const uint32_t lo = (uint32_t)bf16_rne(a0) | ((uint32_t)bf16_rne(a1) << 16);
+        const uint32_t hi = (uint32_t)bf16_rne(a2) | ((uint32_t)bf16_rne(a3) << 16);
+        *reinterpret_cast<uint2*>(y + (size_t)t * H + c) = make_uint2(lo, hi);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Weight preparation
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prep_amax_kernel(const float* __restrict__ w,
+                                                        size_t per_expert,
+                                                        uint32_t* __restrict__ amax) {
+    const int e = blockIdx.y;
+    const float* we = w + (size_t)e * per_expert;
+    float m = 0.0f;
+    for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < per_expert;
+         i += (size_t)gridDim.x * 256 * 4) {
+        const float4 q = *reinterpret_cast<const float4*>(we + i);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))));
+    }
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(amax + e, f2u(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
+// Logical row of prepared row p (SwiGLU strip interleave when swiglu_I > 0).
+__device__ __forceinline__ int logical_row(int p, int swiglu_I) {
+    if (!swiglu_I) return p;
+    const int st = p >> 4;
+    return (st & 1) * swiglu_I + (st >> 1) * 16 + (p & 15);
+}
+
+// One thread per (expert, prepared row, 16-block): quantize with the expert's
+// global scale and scatter into the micro-tile register image.
+__global__ __launch_bounds__(256) void prep_nvfp4_kernel(const float* __restrict__ w, int E, int N,
+                                                         int K, int swiglu_I,
+                                                         const uint32_t* __restrict__ amax,
+                                                         float* __restrict__ gout,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+    const int nkb = K / 16;
+    const size_t total = (size_t)E * N * nkb;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int e = (int)(id / ((size_t)N * nkb));
+    const int rem = (int)(id % ((size_t)N * nkb));
+    const int p = rem / nkb, kb = rem % nkb;
+    const float g = __fdiv_rn(u2f(amax[e]), 2688.0f);
+    if (p == 0 && kb == 0) gout[e] = g;
+    const int n = logical_row(p, swiglu_I);
+    float v[16];
+    const float4* src = reinterpret_cast<const float4*>(w + ((size_t)e * N + n) * K + (size_t)kb * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float4 q = src[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+    uint32_t packed[2], sf;
+    nvfp4_block(v, g, packed, &sf);
+    const int k0 = kb * 16, kt = k0 / kTileK, j = (k0 % kTileK) / 32, half = (k0 % 32) / 16;
+    const size_t tiles_e = (size_t)(N / kStrip) * (K / kTileK);
+    const size_t tile = (size_t)e * tiles_e + (size_t)(p / kStrip) * (K / kTileK) + kt;
+    uint8_t* cb = codes + tile * kNvTileBytes;
+    const int l1 = (p & 15) + 16 * (2 * half), l2 = l1 + 16;
+    *reinterpret_cast<uint32_t*>(cb + l1 * 16 + j * 4) = packed[0];
+    *reinterpret_cast<uint32_t*>(cb + l2 * 16 + j * 4) = packed[1];
+    scales[tile * kNvTileScale + (half * 16 + (p & 15)) * 4 + j] = (uint8_t)sf;
+}
+
+// One thread per (expert, prepared row, 32-block).
+__global__ __launch_bounds__(256) void prep_mxfp8_kernel(const float* __restrict__ w, int E, int N,
+                                                         int K, int swiglu_I,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+    const int nkb = K / 32;
+    const size_t total = (size_t)E * N * nkb;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int e = (int)(id / ((size_t)N * nkb));
+    const int rem = (int)(id % ((size_t)N * nkb));
+    const int p = rem / nkb, kb = rem % nkb;
+    const int n = logical_row(p, swiglu_I);
+    float v[32];
+    const float4* src = reinterpret_cast<const float4*>(w + ((size_t)e * N + n) * K + (size_t)kb * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 q = src[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+    }
+    uint8_t c[32];
+    const uint32_t e8 = mxfp8_block(v, c);
+    const int k0 = kb * 32, kt = k0 / kTileK, kb4 = (k0 % kTileK) / 32;
+    const size_t tiles_e = (size_t)(N / kStrip) * (K / kTileK);
+    const size_t tile = (size_t)e * tiles_e + (size_t)(p / kStrip) * (K / kTileK) + kt;
+    uint8_t* cb = codes + tile * kF8TileBytes;
+    // block kb4 covers tile k in [32 kb4, 32 kb4 + 32): its first 16 values
+    // live in lane q = (32 kb4 mod 64)/16, byte offset (kb4 >= 2 ? 16 : 0), the
+    // next 16 in lane q + 1 at the same byte offset.
+    const int q0 = ((32 * kb4) % 64) / 16, boff = kb4 >= 2 ? 16 : 0;
+    const int la = (p & 15) + 16 * q0, lb = la + 16;
+    *reinterpret_cast<uint4*>(cb + la * 32 + boff) = *reinterpret_cast<const uint4*>(c);
+    *reinterpret_cast<uint4*>(cb + lb * 32 + boff) = *reinterpret_cast<const uint4*>(c + 16);
+    scales[tile * kF8TileScale + (p & 15) + 16 * kb4] = (uint8_t)e8;
+}
+
+__global__ void write_header_kernel(BlobHeader h, uint32_t* __restrict__ dst) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&h);
+    if (threadIdx.x < sizeof(BlobHeader) / 4) dst[threadIdx.x] = w[threadIdx.x];
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(size_t n, unsigned cap = 4096) {
+    size_t g = (n + 255) / 256;
+    if (g > cap) g = cap;
+    return g ? (unsigned)g : 1u;
+}
+
+hipError_t launch_write_header(const BlobHeader& h, void* dst, hipStream_t s) {
+    hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, s, h, static_cast<uint32_t*>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, hipStream_t s) {
+    if (in_bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid_for(n, 2048)), dim3(256), 0, s, v, n, slot);
+    else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid_for(n, 2048)), dim3(256), 0, s, v, n, slot);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
+                             const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
+                             uint16_t* deq, hipStream_t s) {
+    const dim3 grid((rows + 3) / 4), block(256);
+#define QR(KD, BF) hipLaunchKernelGGL((quant_rows_kernel<KD, BF>), grid, block, 0, s, v, rows, cols, amax_slot, codes, scales, g, deq)
+    if (in_bf16) {
+        if (kind == QK_NV_TENSOR) QR(QK_NV_TENSOR, true);
+        else if (kind == QK_NV_ROW) QR(QK_NV_ROW, true);
+        else QR(QK_MX, true);
+    } else {
+        if (kind == QK_NV_TENSOR) QR(QK_NV_TENSOR, false);
+        else if (kind == QK_NV_ROW) QR(QK_NV_ROW, false);
+        else QR(QK_MX, false);
+    }
+#undef QR
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 8192)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, hipStream_t s) {
+    hipLaunchKernelGGL(yacc_to_bf16_kernel, dim3(grid_for(n, 8192)), dim3(256), 0, s, yacc, n, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const void* O, int is_bf16, const int32_t* rt2row, const float* w,
+                           int T, int K, int H, uint16_t* y, hipStream_t s) {
+    if (is_bf16) hipLaunchKernelGGL(finalize_kernel<true>, dim3(T), dim3(256), 0, s, O, rt2row, w, K, H, y);
+    else hipLaunchKernelGGL(finalize_kernel<false>, dim3(T), dim3(256), 0, s, O, rt2row, w, K, H, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_amax(const float* w, int E, size_t per_expert, uint32_t* amax, hipStream_t s) {
+    unsigned gx = (unsigned)((per_expert / 4 + 255) / 256);
+    if (gx > 256) gx = 256;
+    if (gx == 0) gx = 1;
+    hipLaunchKernelGGL(prep_amax_kernel, dim3(gx, E), dim3(256), 0, s, w, per_expert, amax);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_nvfp4(const float* w, int E, int N, int K, int swiglu_I,
+                             const uint32_t* amax, float* g, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s) {
+    const size_t total = (size_t)E * N * (K / 16);
+    hipLaunchKernelGGL(prep_nvfp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       w, E, N, K, swiglu_I, amax, g, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_mxfp8(const float* w, int E, int N, int K, int swiglu_I, uint8_t* codes,
+                             uint8_t* scales, hipStream_t s) {
+    const size_t total = (size_t)E * N * (K / 32);
+    hipLaunchKernelGGL(prep_mxfp8_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       w, E, N, K, swiglu_I, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace moe

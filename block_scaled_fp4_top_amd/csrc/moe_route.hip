@@ -1,0 +1,203 @@
+// S1 routing (top-K + renormalised softmax) and S2 expert-contiguous
+// permutation (MegaMoE post, "The problem": tokens go to a top-K subset of
+// experts and the grouped GEMMs consume them expert by expert).
+#include "moe_internal.h"
+#include "moe_kernels.h"
+
+namespace moe {
+
+// One wave per token, 4 tokens per block. Each lane holds E/64 logits; K
+// rounds of a wave-wide (max value, min index) reduction pick the experts in
+// descending order with ties to the lower id. Lane k keeps the k-th pick.
+// p_k = exp(l_k - l_max) / sum_j exp(l_j - l_max), summed in k order.
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ topw,
+                                                         uint32_t* __restrict__ misc) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) misc[threadIdx.x] = 0u;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float v[EPL];
+    const float* lt = logits + (size_t)t * E;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        v[i] = e < E ? lt[e] : 0.0f;
+    }
+    uint32_t taken = 0;
+    float my_v = 0.0f;
+    int my_e = 0;
+    for (int k = 0; k < K; ++k) {
+        float bv = 0.0f;
+        int be = 0x7FFFFFFF;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((taken >> i) & 1u)) {
+                if (be == 0x7FFFFFFF || v[i] > bv) { bv = v[i]; be = e; }
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oe = __shfl_xor(be, off);
+            const bool take = (be == 0x7FFFFFFF) ||
+                              (oe != 0x7FFFFFFF && (ov > bv || (ov == bv && oe < be)));
+            if (take) { bv = ov; be = oe; }
+        }
+        if ((be & 63) == lane) taken |= 1u << (be >> 6);
+        if (lane == k) { my_v = bv; my_e = be; }
+    }
+    const float m = __shfl(my_v, 0);
+    const float ex = lane < K ? expf(my_v - m) : 0.0f;
+    float s = 0.0f;
+    for (int k = 0; k < K; ++k) s += __shfl(ex, k);
+    if (lane < K) {
+        ids[(size_t)t * K + lane] = my_e;
+        topw[(size_t)t * K + lane] = __fdiv_rn(ex, s);
+    }
+}
+
+// Per-block expert histogram of kPermChunk consecutive routes (LDS atomics;
+// counts do not depend on the order of the increments).
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ ids, int R,
+                                                        int E, int32_t* __restrict__ bhist) {
+    __shared__ int32_t h[kMaxE];
+    for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+    __syncthreads();
+    const int base = blockIdx.x * kPermChunk;
+    for (int i = threadIdx.x; i < kPermChunk; i += 256) {
+        const int r = base + i;
+        if (r < R) atomicAdd(&h[ids[r]], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) bhist[(size_t)blockIdx.x * E + e] = h[e];
+}
+
+// Exclusive scan over 1024 threads in LDS (Hillis-Steele, double buffered).
+__device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*[2][1024]*/) {
+    const int t = threadIdx.x;
+    int src = 0;
+    buf[t] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int x = buf[src * 1024 + t] + (t >= off ? buf[src * 1024 + t - off] : 0);
+        buf[(1 - src) * 1024 + t] = x;
+        src = 1 - src;
+        __syncthreads();
+    }
+    const int incl = buf[src * 1024 + t];
+    __syncthreads();
+    return incl - v;
+}
+
+// One block of 1024 threads (thread e = expert e): per-block bases by a
+// column scan over the block histograms, expert counts and offsets, and the
+// exclusive scans of ceil(count / BM) that list the grouped-GEMM M-tiles.
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ bhist,
+                                                         int nblk, int E, int R,
+                                                         int32_t* __restrict__ bbase,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ tiles) {
+    __shared__ int buf[2 * 1024];
+    const int e = threadIdx.x;
+    int run = 0;
+    if (e < E) {
+        for (int b = 0; b < nblk; ++b) {
+            bbase[(size_t)b * E + e] = run;
+            run += bhist[(size_t)b * E + e];
+        }
+    }
+    const int off = block1024_exclusive_scan(e < E ? run : 0, buf);
+    if (e < E) {
+        counts[e] = run;
+        offsets[e] = off;
+        for (int b = 0; b < nblk; ++b) bbase[(size_t)b * E + e] += off;
+    }
+    if (e == 0) offsets[E] = R;
+#pragma unroll
+    for (int i = 0; i < kNumBM; ++i) {
+        const int bm = bm_of(i);
+        const int nt = e < E ? (run + bm - 1) / bm : 0;
+        const int toff = block1024_exclusive_scan(nt, buf);
+        if (e < E) tiles[i * (E + 1) + e] = toff;
+        if (e == E - 1) tiles[i * (E + 1) + E] = toff + nt;
+    }
+}
+
+// Scatter: route r gets row bbase[block][e] + (routes of expert e earlier in
+// this block). Sub-chunks of 256 routes are processed in order; inside a wave
+// the rank comes from ballots matching the expert id bit by bit; across the
+// block's waves from per-wave counts in LDS. No atomics decide any position.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ ids, int R,
+                                                           int E, const int32_t* __restrict__ bbase,
+                                                           int32_t* __restrict__ r2r,
+                                                           int32_t* __restrict__ rt2row) {
+    __shared__ int32_t cnt[kMaxE];
+    __shared__ int32_t wh[4][kMaxE];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int e = tid; e < E; e += 256) {
+        cnt[e] = bbase[(size_t)blockIdx.x * E + e];
+        wh[0][e] = wh[1][e] = wh[2][e] = wh[3][e] = 0;
+    }
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int sub = 0; sub < kPermChunk / 256; ++sub) {
+        const int r = blockIdx.x * kPermChunk + sub * 256 + tid;
+        const bool valid = r < R;
+        const int x = valid ? ids[r] : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (x >> b) & 1;
+            const uint64_t bal = __ballot(valid && bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+        if (valid && rank == 0) wh[w][x] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int prior = 0;
+            for (int ww = 0; ww < w; ++ww) prior += wh[ww][x];
+            const int row = cnt[x] + prior + rank;
+            if (row >= 0 && row < R) {
+                r2r[row] = r;
+                rt2row[r] = row;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += 256) {
+            cnt[e] += wh[0][e] + wh[1][e] + wh[2][e] + wh[3][e];
+            wh[0][e] = wh[1][e] = wh[2][e] = wh[3][e] = 0;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
+                        uint32_t* misc, hipStream_t s) {
+    const dim3 grid((T + 3) / 4), block(256);
+    const int epl = (E + 63) / 64;
+    if (epl <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    else if (epl <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    else if (epl <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    else if (epl <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* bhist,
+                          int32_t* bbase, int32_t* counts, int32_t* offsets, int32_t* tiles,
+                          int32_t* r2r, int32_t* rt2row, hipStream_t s) {
+    hipLaunchKernelGGL(perm_hist_kernel, dim3(nblk), dim3(256), 0, s, ids, R, E, bhist);
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, bhist, nblk, E, R, bbase,
+                       counts, offsets, tiles);
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(256), 0, s, ids, R, E, bbase, r2r,
+                       rt2row);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,165 @@
+/*
+ * moe_fp4: one block-scaled Mixture-of-Experts layer forward on an AMD MI355X
+ * (gfx950), as a C ABI.
+ *
+ * What is computed (MegaMoE post, flashinfer.ai, "The problem" and "Our
+ * approach"; FlashInfer PR #4366, "Description"; newruntime summary of
+ * FlashInfer PR #5319, "Retrieval answer"):
+ *
+ *   S1 route     per token, the top-K of E router logits (descending, ties to
+ *                the lower expert id) and weights p = softmax over the chosen K;
+ *   S2 permute   routes r = t*K + k grouped by expert, tokens ascending inside a
+ *                group (expert-contiguous grouped-GEMM order);
+ *   S3 quantize  FC1 input: NVFP4 (E2M1 values, E4M3 scale per 16 elements,
+ *                FP32 global scale per tensor or per token), MXFP8 (E4M3 values,
+ *                E8M0 scale per 32) or none (W4A16: bf16 activations);
+ *   S4 FC1       grouped GEMM h = x W1_e^T per route;
+ *   S5           SwiGLU (silu(gate) * up) or ReLU2 (max(h,0)^2); with input-side
+ *                placement the result is multiplied by p in FP32; then the FC2
+ *                input is quantized (W4A4: NVFP4 per tensor or per route; MXFP8)
+ *                or stored as bf16 (W4A16);
+ *   S6 FC2       grouped GEMM o = a W2_e^T per route;
+ *   S7 finalize  y[t] = sum_k w[t,k] o[route t*K+k] with w = p (output side) or
+ *                1 (input side, the weight was applied before FC2), either in
+ *                fixed k order (deterministic) or fused into FC2 by atomics.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are device pointers (hipMalloc'd or equivalent), row-major,
+ *    owned by the caller. The library never allocates device or host memory
+ *    and keeps no per-call state, except the optional stage timing below.
+ *  - Every call only enqueues work on `stream` and returns; no host<->device
+ *    synchronisation except in moe_check_prepared and moe_stage_times.
+ *  - Argument checks all run before any launch; on failure nothing is
+ *    enqueued and a moe_status other than MOE_OK is returned, with a message in
+ *    moe_last_error().
+ *  - Device pointers must be 256-byte aligned where noted, else 16-byte aligned.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_W4A4_TENSOR = 0, /* NVFP4 weights and activations, one activation global scale per tensor */
+    MOE_W4A4_TOKEN = 1,  /* NVFP4 weights and activations, one activation global scale per row    */
+    MOE_W4A16 = 2,       /* NVFP4 weights, bf16 activations                                         */
+    MOE_MXFP8 = 3        /* MXFP8 (E4M3 + E8M0 per 32) weights and activations                      */
+} moe_mode;
+
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
+typedef enum { MOE_FMT_NVFP4 = 0, MOE_FMT_MXFP8 = 1 } moe_wfmt;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID = 1,     /* null/misaligned pointer, bad size or enum                  */
+    MOE_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. H % 128 != 0)       */
+    MOE_ERR_WORKSPACE = 3,   /* workspace or prepared buffer too small                      */
+    MOE_ERR_HIP = 4          /* a HIP call failed; moe_last_error() has hipGetErrorString */
+} moe_status;
+
+/* Layer geometry. N1 = 2*I for SwiGLU (rows [0,I) gate, [I,2I) up), I for
+ * ReLU2. Limits: 1 <= E <= 1024; H and I positive multiples of 128 (the K
+ * extent of one weight micro-tile); H, I <= 32768. */
+typedef struct {
+    int32_t E, H, I;
+    int32_t act;  /* moe_act  */
+    int32_t wfmt; /* moe_wfmt */
+} moe_dims;
+
+/* Size in bytes of the prepared-weight blob for `d` (0 if `d` is invalid). */
+size_t moe_prepared_bytes(const moe_dims* d);
+
+/* S0 (off the timed path): quantize and reorder the weights.
+ * Weights arrive in the standard checkpoint layout and the library quantizes
+ * and reorders them itself (MegaMoE post, "Usage"); one NVFP4 blob serves the
+ * W4A4 and W4A16 modes (newruntime summary of PR #5319, title).
+ *   w1: [E][N1][H] fp32, w2: [E][H][I] fp32 (device).
+ *   prepared: device buffer of at least moe_prepared_bytes(d) bytes, 256-byte
+ *   aligned; written entirely (header, per-expert FP32 global scales
+ *   g = amax / (6*448) per expert per matrix for NVFP4, codes and scales in the
+ *   kernel-native layout described in the design notes). Immutable afterwards;
+ *   it may be shared by concurrent forwards. */
+int moe_prepare_weights(const moe_dims* d, const float* w1, const float* w2, void* prepared,
+                        size_t prepared_bytes, hipStream_t stream);
+
+/* Synchronous check that a device blob's header matches `d` (reads 256 bytes
+ * to the host; not for use under graph capture). */
+int moe_check_prepared(const moe_dims* d, const void* prepared, hipStream_t stream);
+
+/* Workspace bytes needed by moe_forward for up to T_max tokens and top-K. */
+size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t mode);
+
+/* S1..S7: one layer forward.
+ *   prepared: blob from moe_prepare_weights with the same `d` (NVFP4 blob for
+ *             modes 0..2, MXFP8 blob for mode 3).
+ *   x:        [T][H] bf16 bit patterns.            logits: [T][E] fp32 (finite).
+ *   T >= 1, 1 <= K <= min(E, 64).
+ *   act must equal d->act. router_weight_on_input: 0 = output side (finalize
+ *   weights p), 1 = input side (p applied to the FP32 activation output before
+ *   the FC2-input quantization or bf16 store; finalize weights 1).
+ *   deterministic_finalize: 1 = fixed-order unpermute+reduce (bit-identical run
+ *   to run), 0 = fused scatter-add in the FC2 epilogue (fp32 atomics; the
+ *   summation order, hence the last bits, may vary run to run).
+ *   workspace: >= moe_workspace_bytes(d, T, K, mode) bytes, 256-byte aligned;
+ *   afterwards it holds the intermediate views listed by moe_workspace_view.
+ *   y: [T][H] bf16 bit patterns (output). */
+int moe_forward(const moe_dims* d, const void* prepared, const uint16_t* x, const float* logits,
+                int32_t T, int32_t K, int32_t mode, int32_t act, int32_t router_weight_on_input,
+                int32_t deterministic_finalize, void* workspace, size_t workspace_bytes,
+                uint16_t* y, hipStream_t stream);
+
+/* S7 alone (unfused finalize, as in PR #5319): y[t][j] = sum_{k<K} w[t][k] *
+ * permuted_out[route_to_row[t*K+k]][j], accumulated in fp32 in k order and
+ * rounded once to bf16.
+ *   permuted_out: [R][H] fp32 (out_is_bf16 = 0) or bf16 (1), R = T*K.
+ *   route_to_row: [T*K] int32, each in [0, R).  weights: [T][K] fp32 or NULL
+ *   for unit weights (input-side placement).  y: [T][H] bf16. */
+int moe_finalize(const void* permuted_out, int32_t out_is_bf16, const int32_t* route_to_row,
+                 const float* weights, int32_t T, int32_t K, int32_t H, uint16_t* y,
+                 hipStream_t stream);
+
+/* Standalone block quantizer (the S3/S5 quantizer as a library call).
+ *   v: [rows][cols] fp32; kind: 0 = NVFP4 one global scale for the whole
+ *   matrix, 1 = NVFP4 one global scale per row, 2 = MXFP8.
+ *   codes: NVFP4 [rows][cols/2] (two E2M1 codes per byte, even element in the
+ *   low nibble); MXFP8 [rows][cols] E4M3.  scales: NVFP4 [rows][cols/16] E4M3;
+ *   MXFP8 [rows][cols/32] E8M0.  g: NVFP4 [1] or [rows] fp32 (unused for MXFP8).
+ *   scratch: 256 bytes of device memory (cleared by the call).
+ *   cols % 32 == 0. */
+int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8_t* codes,
+                 uint8_t* scales, float* g, void* scratch, hipStream_t stream);
+
+/* Location of an intermediate inside the workspace (for inspection/parity):
+ *   0 topk_ids [T][K] i32        1 topk_w [T][K] f32
+ *   2 counts [E] i32             3 offsets [E+1] i32
+ *   4 row_to_route [R] i32       5 route_to_row [R] i32
+ *   6 x codes                    7 x scales               8 x global scale(s) f32
+ *   9 FC2 input, fp32 before quantization [R][I] (W4A4, MXFP8) or bf16 (W4A16)
+ *   10 FC2-input codes           11 FC2-input scales      12 FC2-input global scale(s)
+ *   13 permuted FC2 output O [R][H] f32 (deterministic finalize)
+ * Returns MOE_ERR_INVALID for a view the mode does not produce. */
+int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32_t mode, int32_t view_id,
+                       size_t* offset, size_t* bytes);
+
+/* Optional per-stage timing with HIP events recorded on the forward's stream
+ * around each stage (not to be enabled under graph capture). moe_stage_times
+ * synchronises, returns the summed milliseconds per stage since the last
+ * reset in ms[0..n) and the number of timed forwards, and resets. Stage ids:
+ * 0 route, 1 permute, 2 quantize x, 3 FC1, 4 FC2-input quantize, 5 FC2,
+ * 6 finalize. */
+int moe_stage_timing(int32_t enable);
+int moe_stage_times(float* ms, int32_t n, int32_t* forwards);
+
+/* Message for the last non-OK status returned on this thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FP4_H */

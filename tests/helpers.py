@@ -1,0 +1,182 @@
+"""Shared helpers for the GPU parity tests: seeded inputs, the oracle run, blob
+unpacking (host logic) and the comparison bars."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import reference as R
+from synth_inputs import make_expert_weights, make_logits, make_x
+from synth_inputs.gen import STREAM_W1, STREAM_W2, make_weight
+
+# Output bar: max|err| <= 2e-2 * rms(ref) and ||err||_F / ||ref||_F <= 1e-2,
+# with the GPU's bf16 output compared against the unrounded fp64 oracle.
+MAX_ERR_RMS = 2e-2
+REL_FRO = 1e-2
+TOPW_REL = 1e-6
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().float().numpy().astype(np.float64)
+
+
+def out_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
+    err = y_gpu - y_ref
+    rms = math.sqrt(float(np.mean(y_ref * y_ref)))
+    max_rel = float(np.max(np.abs(err))) / rms
+    fro = float(np.linalg.norm(err) / np.linalg.norm(y_ref))
+    return max_rel, fro
+
+
+def assert_output_close(y_gpu: np.ndarray, y_ref: np.ndarray, what=""):
+    max_rel, fro = out_errors(y_gpu, y_ref)
+    assert max_rel <= MAX_ERR_RMS and fro <= REL_FRO, \
+        f"{what}: max|err|/rms={max_rel:.3e} (bar {MAX_ERR_RMS}), rel Frobenius={fro:.3e} (bar {REL_FRO})"
+    return max_rel, fro
+
+
+class Inputs:
+    """Seeded inputs of one workload shape, generated on `gen_device` and
+    mirrored to the other side so that the oracle and the GPU read identical
+    bytes."""
+
+    def __init__(self, T, H, I, E, K, act, logits_kind, seed=0, gen_device="cpu",
+                 make_weights=True):
+        self.T, self.H, self.I, self.E, self.K, self.act = T, H, I, E, K, act
+        self.N1 = 2 * I if act == "swiglu" else I
+        self.seed = seed
+        self.x = make_x(seed, T, H, device=gen_device).cuda()
+        self.logits = make_logits(seed, T, E, logits_kind, device=gen_device).cuda()
+        self.w1 = self.w2 = None
+        if make_weights:
+            if gen_device == "cpu":
+                w1, w2 = make_expert_weights(seed, E, self.N1, H, I)
+                self.w1, self.w2 = w1.cuda(), w2.cuda()
+            else:
+                self.w1 = torch.empty((E, self.N1, H), dtype=torch.float32, device="cuda")
+                self.w2 = torch.empty((E, H, I), dtype=torch.float32, device="cuda")
+                for e in range(E):
+                    self.w1[e] = make_weight(seed, STREAM_W1, e, self.N1, H, device="cuda")
+                    self.w2[e] = make_weight(seed, STREAM_W2, e, H, I, device="cuda")
+
+    def x_bits(self):
+        return bits16(self.x)
+
+    def logits_np(self):
+        return self.logits.cpu().numpy()
+
+    def provider(self, e):
+        return self.w1[e].cpu().numpy(), self.w2[e].cpu().numpy()
+
+    def oracle_weights(self, fmt):
+        return R.QuantWeights(fmt, self.E, self.H, self.I, self.act, self.provider)
+
+
+# ---------------------------------------------------------------------------
+# blob unpacking (layout documented in csrc/moe_internal.h)
+# ---------------------------------------------------------------------------
+HEADER_FIELDS = ["magic0", "magic1", "version", "wfmt", "E", "H", "I", "N1", "act", "pad0"]
+
+
+def blob_header(blob: np.ndarray) -> dict:
+    w = blob[:40].view(np.uint32)
+    h = dict(zip(HEADER_FIELDS, [int(v) for v in w]))
+    offs = blob[40:40 + 64].view(np.uint64)
+    for k, v in zip(["off_g1", "off_g2", "off_amax", "off_w1", "off_s1", "off_w2", "off_s2",
+                     "total"], offs):
+        h[k] = int(v)
+    return h
+
+
+def _logical_rows(N, swiglu_I):
+    p = np.arange(N)
+    if not swiglu_I:
+        return p
+    st = p >> 4
+    return (st & 1) * swiglu_I + (st >> 1) * 16 + (p & 15)
+
+
+def unpack_nvfp4_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: int, swiglu_I=0):
+    """Blob bytes of one expert's NVFP4 matrix -> (codes [N][K], scales [N][K/16])
+    in logical (checkpoint) order."""
+    NT, KT = N // 16, K // 128
+    t = codes_b.reshape(NT, KT, 64, 4, 4)           # tile, lane, dword j, byte
+    lo, hi = t & 15, t >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(NT, KT, 64, 4, 8)  # element e = 2*byte + half
+    lane = np.arange(64)
+    out = np.empty((N, K), np.uint8)
+    for j in range(4):
+        for q in range(4):
+            ls = lane[q * 16:(q + 1) * 16]
+            # rows nt*16 + ls%16, k = kt*128 + 32 j + 8 q + e
+            blk = nib[:, :, ls, j, :]                # NT, KT, 16, 8
+            blk = blk.transpose(0, 2, 1, 3)          # NT, 16, KT, 8
+            for e in range(8):
+                out.reshape(NT, 16, KT, 128)[:, :, :, 32 * j + 8 * q + e] = blk[..., e]
+    s = scales_b.reshape(NT, KT, 2, 16, 4)          # par, row, byte j
+    sc = np.empty((N, K // 16), np.uint8)
+    scv = sc.reshape(NT, 16, KT, 8)
+    for par in range(2):
+        for j in range(4):
+            scv[:, :, :, 2 * j + par] = s[:, :, par, :, j].transpose(0, 2, 1)
+    rows = _logical_rows(N, swiglu_I)
+    outl = np.empty_like(out)
+    scl = np.empty_like(sc)
+    outl[rows] = out
+    scl[rows] = sc
+    return outl, scl
+
+
+def unpack_mxfp8_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: int, swiglu_I=0):
+    NT, KT = N // 16, K // 128
+    t = codes_b.reshape(NT, KT, 4, 16, 32)          # tile, q, row, byte
+    out = np.empty((N, K), np.uint8)
+    ov = out.reshape(NT, 16, KT, 128)
+    for q in range(4):
+        blk = t[:, :, q].transpose(0, 2, 1, 3)      # NT, 16, KT, 32
+        ov[:, :, :, 16 * q:16 * q + 16] = blk[..., :16]
+        ov[:, :, :, 64 + 16 * q:64 + 16 * q + 16] = blk[..., 16:]
+    s = scales_b.reshape(NT, KT, 4, 16)             # block, row
+    sc = np.empty((N, K // 32), np.uint8)
+    scv = sc.reshape(NT, 16, KT, 4)
+    for b in range(4):
+        scv[:, :, :, b] = s[:, :, b, :].transpose(0, 2, 1)
+    rows = _logical_rows(N, swiglu_I)
+    outl = np.empty_like(out)
+    scl = np.empty_like(sc)
+    outl[rows] = out
+    scl[rows] = sc
+    return outl, scl
+
+
+def unpack_expert(blob: np.ndarray, e: int):
+    """(W1 codes, W1 scales, g1, W2 codes, W2 scales, g2) of expert e."""
+    h = blob_header(blob)
+    E, H, I, N1 = h["E"], h["H"], h["I"], h["N1"]
+    nv = h["wfmt"] == 0
+    tb, sb = (1024, 128) if nv else (2048, 64)
+    t1 = (N1 // 16) * (H // 128)
+    t2 = (H // 16) * (I // 128)
+    sw = I if h["act"] == 0 else 0
+    c1 = blob[h["off_w1"] + e * t1 * tb: h["off_w1"] + (e + 1) * t1 * tb]
+    s1 = blob[h["off_s1"] + e * t1 * sb: h["off_s1"] + (e + 1) * t1 * sb]
+    c2 = blob[h["off_w2"] + e * t2 * tb: h["off_w2"] + (e + 1) * t2 * tb]
+    s2 = blob[h["off_s2"] + e * t2 * sb: h["off_s2"] + (e + 1) * t2 * sb]
+    g1 = blob[h["off_g1"] + 4 * e: h["off_g1"] + 4 * e + 4].view(np.float32)[0]
+    g2 = blob[h["off_g2"] + 4 * e: h["off_g2"] + 4 * e + 4].view(np.float32)[0]
+    unpack = unpack_nvfp4_matrix if nv else unpack_mxfp8_matrix
+    w1c, w1s = unpack(c1, s1, N1, H, sw)
+    w2c, w2s = unpack(c2, s2, H, I, 0)
+    return w1c, w1s, g1, w2c, w2s, g2
+
+
+def unpack_nibbles(packed: np.ndarray, n: int) -> np.ndarray:
+    """[rows][n/2] packed E2M1 bytes (even element in the low nibble) -> [rows][n]."""
+    p = packed.reshape(-1, n // 2)
+    return np.stack([p & 15, p >> 4], axis=-1).reshape(-1, n)
