@@ -173,6 +173,7 @@ def main():
     for det in (True, False):
         if det is False and "fused" not in wl.finalize:
             continue
+        # eager pass: per-stage HIP events on the launch stream
         for i in range(args.warmup):
             step(i, det)
         torch.cuda.synchronize()
@@ -183,15 +184,39 @@ def main():
         for i in range(args.steps):
             step(i, det)
         torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
+        dt_eager = time.perf_counter() - t0
         moe.stage_timing(False)
         st, nfw = moe.stage_times()
-        results[det] = (dt / args.steps * 1e3, {k: v / max(nfw, 1) for k, v in st.items()})
+        # graph pass: one captured forward per weight copy, replayed in turn
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(copies):
+                step(i, det)
+            torch.cuda.synchronize()
+            for i in range(copies):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    moe.forward(d, blobs[i], x, logits, wl.K, wl.mode, wl.on_input, det,
+                                workspace=ws, out=y, stream=side)
+                graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        dt_graph = time.perf_counter() - t0
+        results[det] = (dt_graph / args.steps * 1e3, dt_eager / args.steps * 1e3,
+                        {k: v / max(nfw, 1) for k, v in st.items()})
+        del graphs
 
     counts = moe.workspace_view(d, ws, wl.T, wl.K, wl.mode, "counts").cpu().numpy()
     touched, wb1, wb2 = touched_bytes(d, counts, wl.wfmt)
     R_ = wl.T * wl.K
-    act_bytes = 2 if wl.mode == "w4a16" else 1
     # algorithmic bytes per launch (see the design notes): weights of the
     # touched experts, the kernel's activation input once, its output once
     x_in = wl.T * wl.H * (2 if wl.mode == "w4a16" else (1 if wl.mode == "mxfp8" else 0.5 + 1 / 16))
@@ -202,7 +227,7 @@ def main():
     bytes_fc2 = wb2 + fc2_in + fc2_out
     flops_fc1 = 2.0 * R_ * wl.N1 * wl.H
     flops_fc2 = 2.0 * R_ * wl.H * wl.I
-    ms_det, st_det = results[True] if True in results else results[False]
+    ms_det, ms_eager, st_det = results[True] if True in results else results[False]
     kernel = "fc1" if st_det["fc1"] >= st_det["fc2"] else "fc2"
     kms = st_det[kernel]
     kbytes = bytes_fc1 if kernel == "fc1" else bytes_fc2
@@ -240,17 +265,21 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
                    "K": wl.K, "mode": wl.mode, "act": wl.act,
-                   "router_weight_on_input": wl.on_input, "finalize": "deterministic",
+                   "router_weight_on_input": wl.on_input,
+                   "finalize": "deterministic" if True in results else "fused",
+                   "timing": "hipGraph replay of one forward per step",
                    "weight_copies_rotated": copies, "touched_experts": touched},
+        "eager_ms_per_step": round(ms_eager, 5),
         "stages_us": {k: round(v * 1e3, 2) for k, v in st_det.items()},
         "layer_tflops": round((flops_fc1 + flops_fc2) / (ms_det * 1e-3) / 1e12, 2),
         "layer_weight_gbs": round((wb1 + wb2) / (ms_det * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
     if False in results and True in results:
-        ms_f, st_f = results[False]
+        ms_f, ms_fe, st_f = results[False]
         out["fused_finalize"] = {"value": round(wl.T / (ms_f * 1e-3), 1),
                                  "ms_per_step": round(ms_f, 5),
+                                 "eager_ms_per_step": round(ms_fe, 5),
                                  "stages_us": {k: round(v * 1e3, 2) for k, v in st_f.items()}}
     out["cpu_baseline"] = None
     if cpu_w is not None:

@@ -294,8 +294,13 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     timer_mark(0, stream);
     HIP_TRY(launch_route(logits, T, E, K, ids, topw, misc, stream), "route");
     timer_mark(1, stream);
-    HIP_TRY(launch_permute(ids, R, E, P.nblk, bhist, bbase, counts, offsets, tiles, r2r, rt2row, stream),
-            "permute");
+    if (small_route_permute(R, E)) {
+        HIP_TRY(launch_permute_small(ids, R, E, counts, offsets, tiles, r2r, rt2row, stream), "permute");
+    } else {
+        HIP_TRY(launch_permute(ids, R, E, P.nblk, bhist, bbase, counts, offsets, tiles, r2r, rt2row,
+                               stream),
+                "permute");
+    }
     timer_mark(2, stream);
     if (nv4) {
         if (!per_row) HIP_TRY(launch_amax(x, 1, (size_t)T * H, misc + kMiscXAmax, stream), "x amax");

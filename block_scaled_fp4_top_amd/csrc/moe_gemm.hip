@@ -51,18 +51,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     __shared__ int s_arow[BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int id = blockIdx.x;
+    // Block order: M-tile fastest (across experts), then N-block; consecutive
+    // positions go to the same XCD (blocks are dealt round-robin over the 8
+    // XCDs and the grid is a multiple of 8), so concurrently running blocks of
+    // one XCD share an N-block's weight columns.
     const int total = gridDim.x;
-    if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);  // same-XCD neighbours
+    const int id = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
     const int mt = id % p.mt_max, nb = id / p.mt_max;
-    if (mt >= p.tiles[p.E]) return;
+    if (nb >= p.N / (64 * WN) || mt >= p.tiles[p.E]) return;
     int lo = 0, hi = p.E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
     }
     const int e = lo;
-    const int row0 = p.offsets[e] + (mt - p.tiles[e]) * BM;
+    const int mt_local = mt - p.tiles[e];
+    const int row0 = p.offsets[e] + mt_local * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
     for (int m = tid; m < BM; m += 256)
         s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
@@ -273,7 +277,8 @@ template <int AB, int EPI>
 static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s) {
     constexpr int WN = 2;
     const int nbn = a.N / (64 * WN);
-    const dim3 grid((unsigned)(nbn * a.mt_max)), block(256);
+    const long long blocks = (long long)nbn * a.mt_max;
+    const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(256);
     switch (bm_index) {
         case 0: hipLaunchKernelGGL((gemm_kernel<AB, 16, WN, EPI>), grid, block, 0, s, a); break;
         case 1: hipLaunchKernelGGL((gemm_kernel<AB, 32, WN, EPI>), grid, block, 0, s, a); break;

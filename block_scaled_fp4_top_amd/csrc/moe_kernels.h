@@ -9,6 +9,10 @@ namespace moe {
 
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
                         uint32_t* misc, hipStream_t s);
+bool small_route_permute(int R, int E);
+hipError_t launch_permute_small(const int32_t* ids, int R, int E, int32_t* counts,
+                                int32_t* offsets, int32_t* tiles, int32_t* r2r, int32_t* rt2row,
+                                hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* bhist,
                           int32_t* bbase, int32_t* counts, int32_t* offsets, int32_t* tiles,
                           int32_t* r2r, int32_t* rt2row, hipStream_t s);

@@ -55,8 +55,9 @@ __device__ __forceinline__ void nvfp4_deq_f16(const uint32_t* packed, uint32_t s
     }
 }
 
-// One wave per row, 4 rows per block.
-template <int KIND, bool BF16>
+// WPR waves per row: 1 (four rows per block) or 4 (one row per block, for
+// few wide rows).
+template <int KIND, bool BF16, int WPR>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ v, int rows,
                                                          int cols,
                                                          const uint32_t* __restrict__ amax_slot,
@@ -64,13 +65,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
                                                          uint8_t* __restrict__ scales,
                                                          float* __restrict__ g,
                                                          uint16_t* __restrict__ deq) {
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int TPR = 64 * WPR;  // threads per row
+    const int tid = threadIdx.x;
+    const int lt = tid % TPR;      // thread index within the row
+    const int row = blockIdx.x * (4 / WPR) + tid / TPR;
     if (row >= rows) return;
     const size_t base = (size_t)row * cols;
     if (KIND == QK_MX) {
         const int nb = cols / 32;
-        for (int b = lane; b < nb; b += 64) {
+        for (int b = lt; b < nb; b += TPR) {
             float vv[32];
             load16<BF16>(v, base + (size_t)b * 32, vv);
             load16<BF16>(v, base + (size_t)b * 32 + 16, vv + 16);
@@ -86,16 +89,22 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     float gg;
     if (KIND == QK_NV_TENSOR) {
         gg = __fdiv_rn(u2f(*amax_slot), 2688.0f);
-        if (row == 0 && lane == 0) g[0] = gg;
+        if (row == 0 && lt == 0) g[0] = gg;
     } else {
         float m = 0.0f;
-        for (int i = lane; i < cols; i += 64) m = fmaxf(m, fabsf(load1<BF16>(v, base + i)));
+        for (int i = lt; i < cols; i += TPR) m = fmaxf(m, fabsf(load1<BF16>(v, base + i)));
         m = wave_max(m);
+        if (WPR > 1) {
+            __shared__ float red[4];
+            if ((tid & 63) == 0) red[tid >> 6] = m;
+            __syncthreads();
+            m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        }
         gg = __fdiv_rn(m, 2688.0f);
-        if (lane == 0) g[row] = gg;
+        if (lt == 0) g[row] = gg;
     }
     const int nb = cols / 16;
-    for (int b = lane; b < nb; b += 64) {
+    for (int b = lt; b < nb; b += TPR) {
         float vv[16];
         load16<BF16>(v, base + (size_t)b * 16, vv);
         uint32_t packed[2], sf;
@@ -309,17 +318,20 @@ hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, hip
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
                              const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
                              uint16_t* deq, hipStream_t s) {
-    const dim3 grid((rows + 3) / 4), block(256);
-#define QR(KD, BF) hipLaunchKernelGGL((quant_rows_kernel<KD, BF>), grid, block, 0, s, v, rows, cols, amax_slot, codes, scales, g, deq)
+    const bool wide = rows < 2048 && cols >= 1024;  // few long rows: a block per row
+    const dim3 grid(wide ? rows : (rows + 3) / 4), block(256);
+#define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, codes, scales, g, deq)
+#define QRW(KD, BF) do { if (wide) QR(KD, BF, 4); else QR(KD, BF, 1); } while (0)
     if (in_bf16) {
-        if (kind == QK_NV_TENSOR) QR(QK_NV_TENSOR, true);
-        else if (kind == QK_NV_ROW) QR(QK_NV_ROW, true);
-        else QR(QK_MX, true);
+        if (kind == QK_NV_TENSOR) QRW(QK_NV_TENSOR, true);
+        else if (kind == QK_NV_ROW) QRW(QK_NV_ROW, true);
+        else QRW(QK_MX, true);
     } else {
-        if (kind == QK_NV_TENSOR) QR(QK_NV_TENSOR, false);
-        else if (kind == QK_NV_ROW) QR(QK_NV_ROW, false);
-        else QR(QK_MX, false);
+        if (kind == QK_NV_TENSOR) QRW(QK_NV_TENSOR, false);
+        else if (kind == QK_NV_ROW) QRW(QK_NV_ROW, false);
+        else QRW(QK_MX, false);
     }
+#undef QRW
 #undef QR
     return hipGetLastError();
 }

@@ -11,16 +11,10 @@ namespace moe {
 // descending order with ties to the lower id. Lane k keeps the k-th pick.
 // p_k = exp(l_k - l_max) / sum_j exp(l_j - l_max), summed in k order.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
-                                                         int E, int K, int32_t* __restrict__ ids,
-                                                         float* __restrict__ topw,
-                                                         uint32_t* __restrict__ misc) {
-    if (blockIdx.x == 0 && threadIdx.x < 8) misc[threadIdx.x] = 0u;
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
+__device__ __forceinline__ void route_one_token(const float* __restrict__ lt, int E, int K,
+                                                int lane, int32_t* __restrict__ ids_t,
+                                                float* __restrict__ w_t) {
     float v[EPL];
-    const float* lt = logits + (size_t)t * E;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
@@ -55,9 +49,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     float s = 0.0f;
     for (int k = 0; k < K; ++k) s += __shfl(ex, k);
     if (lane < K) {
-        ids[(size_t)t * K + lane] = my_e;
-        topw[(size_t)t * K + lane] = __fdiv_rn(ex, s);
+        ids_t[lane] = my_e;
+        w_t[lane] = __fdiv_rn(ex, s);
     }
+}
+
+// One wave per token, 4 tokens per block. Each lane holds E/64 logits; K
+// rounds of a wave-wide (max value, min index) reduction pick the experts in
+// descending order with ties to the lower id. Lane k keeps the k-th pick.
+// p_k = exp(l_k - l_max) / sum_j exp(l_j - l_max), summed in k order.
+template <int EPL>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
+                                                         int E, int K, int32_t* __restrict__ ids,
+                                                         float* __restrict__ topw,
+                                                         uint32_t* __restrict__ misc) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) misc[threadIdx.x] = 0u;
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    route_one_token<EPL>(logits + (size_t)t * E, E, K, lane, ids + (size_t)t * K,
+                         topw + (size_t)t * K);
 }
 
 // Per-block expert histogram of kPermChunk consecutive routes (LDS atomics;
@@ -177,6 +188,80 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
     }
 }
 
+
+// Small batches (R <= 16384 routes, E <= 256): histogram, scans and the
+// stable scatter in one block of 1024 threads (16 waves), saving two
+// launches. Same results as the multi-block path: the scatter walks the
+// routes in order, 1024 at a time, with in-wave ballot ranks and per-wave
+// counts in LDS.
+constexpr int kSmallMaxE = 256;
+constexpr int kSmallMaxR = 16384;
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ tiles, int32_t* __restrict__ r2r,
+    int32_t* __restrict__ rt2row) {
+    __shared__ int buf[2 * 1024];
+    __shared__ int32_t cnt[kSmallMaxE];
+    __shared__ int32_t wh[16][kSmallMaxE];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int e = tid; e < kSmallMaxE; e += 1024) cnt[e] = 0;
+    __syncthreads();
+    for (int r = tid; r < R; r += 1024) atomicAdd(&cnt[ids[r]], 1);
+    __syncthreads();
+    const int run = tid < E ? cnt[tid] : 0;
+    const int off = block1024_exclusive_scan(run, buf);
+    if (tid < E) {
+        counts[tid] = run;
+        offsets[tid] = off;
+    }
+    if (tid == 0) offsets[E] = R;
+#pragma unroll
+    for (int i = 0; i < kNumBM; ++i) {
+        const int bm = bm_of(i);
+        const int nt = tid < E ? (run + bm - 1) / bm : 0;
+        const int toff = block1024_exclusive_scan(nt, buf);
+        if (tid < E) tiles[i * (E + 1) + tid] = toff;
+        if (tid == E - 1) tiles[i * (E + 1) + E] = toff + nt;
+    }
+    if (tid < E) cnt[tid] = off;
+    for (int e = tid; e < kSmallMaxE; e += 1024)
+        for (int ww = 0; ww < 16; ++ww) wh[ww][e] = 0;
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int base = 0; base < R; base += 1024) {
+        const int r = base + tid;
+        const bool valid = r < R;
+        const int x = valid ? ids[r] : 0;
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = (x >> b) & 1;
+            const uint64_t bal = __ballot(valid && bit);
+            peers &= bit ? bal : ~bal;
+        }
+        const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+        if (valid && rank == 0) wh[w][x] = __popcll(peers);
+        __syncthreads();
+        if (valid) {
+            int prior = 0;
+            for (int ww = 0; ww < w; ++ww) prior += wh[ww][x];
+            const int row = cnt[x] + prior + rank;
+            if (row >= 0 && row < R) {
+                r2r[row] = r;
+                rt2row[r] = row;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += 1024) {
+            int sum = 0;
+            for (int ww = 0; ww < 16; ++ww) { sum += wh[ww][e]; wh[ww][e] = 0; }
+            cnt[e] += sum;
+        }
+        __syncthreads();
+    }
+}
+
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
                         uint32_t* misc, hipStream_t s) {
     const dim3 grid((T + 3) / 4), block(256);
@@ -186,6 +271,16 @@ hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, 
     else if (epl <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
     else if (epl <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
     else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    return hipGetLastError();
+}
+
+bool small_route_permute(int R, int E) { return R <= kSmallMaxR && E <= kSmallMaxE; }
+
+hipError_t launch_permute_small(const int32_t* ids, int R, int E, int32_t* counts,
+                                int32_t* offsets, int32_t* tiles, int32_t* r2r, int32_t* rt2row,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(1024), 0, s, ids, R, E, counts, offsets,
+                       tiles, r2r, rt2row);
     return hipGetLastError();
 }
 
