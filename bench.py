@@ -57,10 +57,14 @@ def touched_bytes(d, counts, wfmt):
 
 
 def kernel_hash():
+    """Hash of the GEMM device code (moe_gemm.hip up to its host launchers,
+    and the layout/codec header)."""
     h = hashlib.sha256()
-    for f in ("moe_gemm.hip", "moe_internal.h", "moe_kernels.h"):
-        with open(os.path.join(ROOT, "block_scaled_fp4_top_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "block_scaled_fp4_top_amd", "csrc")
+    with open(os.path.join(csrc, "moe_gemm.hip"), "rb") as fh:
+        h.update(fh.read().split(b"// ---- host launchers")[0])
+    with open(os.path.join(csrc, "moe_internal.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

@@ -206,6 +206,17 @@ void timer_begin(hipStream_t s) {
     (void)s;
 }
 
+// Events recorded by a kernel launch itself (its start and end) for the
+// boundaries `stage` and `stage + 1`; null when timing is off.
+void timer_kernel_events(int stage, hipEvent_t* t0, hipEvent_t* t1) {
+    StageTimer& T = g_timer;
+    *t0 = *t1 = nullptr;
+    if (T.cur < 0) return;
+    *t0 = T.ev[T.cur][stage];
+    *t1 = T.ev[T.cur][stage + 1];
+    T.used[T.cur][stage] = T.used[T.cur][stage + 1] = true;
+}
+
 void timer_mark(int stage, hipStream_t s) {
     StageTimer& T = g_timer;
     if (T.cur < 0) return;
@@ -313,7 +324,6 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
                                   WS(uint8_t, V_XSCALES), nullptr, nullptr, stream),
                 "quantize x");
     }
-    timer_mark(3, stream);
 
     const int bmi = pick_bm_index(R, E);
     const int BM = bm_of(bmi);
@@ -346,8 +356,9 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     if (nv4 || f8) g1.out_f32 = WS(float, V_A2F);
     else g1.out_bf16 = WS(uint16_t, V_A2F);
     g1.amax_slot = mode == MOE_W4A4_TENSOR ? misc + kMiscA2Amax : nullptr;
-    HIP_TRY(launch_gemm(ab, EPI_FC1, bmi, g1, stream), "FC1");
-    timer_mark(4, stream);
+    hipEvent_t t0, t1;
+    timer_kernel_events(3, &t0, &t1);
+    HIP_TRY(launch_gemm(ab, EPI_FC1, bmi, g1, stream, t0, t1), "FC1");
 
     if (nv4) {
         HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, per_row ? QK_NV_ROW : QK_NV_TENSOR,
@@ -359,7 +370,6 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
                                   WS(uint8_t, V_A2SCALES), nullptr, nullptr, stream),
                 "quantize FC2 input");
     }
-    timer_mark(5, stream);
 
     if (fused) HIP_TRY(launch_fill_u32(WS(uint32_t, V_YACC), (size_t)T * H, 0u, stream), "zero y_acc");
     GemmArgs g2;
@@ -387,8 +397,8 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     g2.out_f32 = WS(float, V_O);
     g2.yacc = WS(float, V_YACC);
     g2.fused = fused;
-    HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream), "FC2");
-    timer_mark(6, stream);
+    timer_kernel_events(5, &t0, &t1);
+    HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream, t0, t1), "FC2");
 
     if (fused) {
         HIP_TRY(launch_yacc_to_bf16(WS(float, V_YACC), (size_t)T * H, y, stream), "convert y");

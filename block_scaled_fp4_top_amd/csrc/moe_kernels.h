@@ -72,6 +72,8 @@ struct GemmArgs {
     int fused;
 };
 
-hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStream_t s);
+// t0/t1: optional events recorded at the kernel's start and end.
+hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStream_t s,
+                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 }  // namespace moe
