@@ -33,6 +33,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t pack_pair(float lo, float hi, bool bf16) {
     if (bf16) return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
@@ -118,15 +119,42 @@ __device__ __forceinline__ void lds_load4(const void* gsrc, void* lds_base) {
         (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
 }
 
-template <int AB, int BM, int WN, int EPI>
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding and all LDS operations are done (export counter not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Orders the first use of a loaded register after the preceding wait: the
+// empty volatile asm "redefines" the value, so no instruction reading it can
+// be scheduled above the asm (and volatile asm keeps its order).
+__device__ __forceinline__ void reg_fence(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void reg_fence(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Workgroup barrier without the fence __syncthreads() carries (that fence
+// drains every outstanding load, which would serialise the pipeline). The
+// caller waits for the loads that must have landed; the memory clobber keeps
+// the compiler from moving memory accesses across.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Grouped GEMM tile kernel. P-stage software pipeline over 128-deep K steps:
+// while step kt is multiplied, the loads of steps kt+1 .. kt+P-1 are in
+// flight (A into P rotating LDS buffers by direct loads, B into P rotating
+// register sets). Every wave issues the same number L of loads per step
+// (padding loads target a scratch LDS area), so "step kt has landed" is the
+// wait vmcnt <= L*(P-2) followed by a barrier.
+template <int AB, int BM, int WN, int EPI, int P>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     constexpr bool F8 = AB == AB_FP8;
     constexpr bool BF = AB == AB_BF16_NV;
     constexpr int MS = BM / 16;
     constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
     constexpr int A_TILE = BM * A_ROW;
-    __shared__ __attribute__((aligned(1024))) uint8_t sA[2][A_TILE];
-    __shared__ __attribute__((aligned(256))) uint32_t sAsc[2][F8 ? BM : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[P][A_TILE];
+    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][F8 ? BM : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
     __shared__ int s_arow[BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -185,33 +213,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
             r = rr >= 0 ? rr : r_any;
         }
         asrc[i] = abase + (size_t)r * a_row_bytes + koff;
-        adst[i] = (ms < MS) ? blk * 1024 : -1;
+        adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
     }
     const uint8_t* ascsrc = nullptr;
-    if (F8 && wave * 64 < BM) {
-        const int rr = s_arow[wave * 64 + lane < BM ? wave * 64 + lane : 0];
+    if (F8) {
+        const int m = wave * 64 + lane;
+        const int rr = m < BM ? s_arow[m] : -1;
         ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
     }
-    auto issue_a = [&](int kt, int buf) {
+    constexpr int L = AB_PER_WAVE + (F8 ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
+
+    // one step's loads; ks >= KT issues the same number of loads as padding
+    auto issue = [&](int ks, int buf, u32x4* c1, u32x4* c2, uint32_t* sc) {
+        const bool real = ks < KT;
+        const int kk = real ? ks : KT - 1;
 #pragma unroll
         for (int i = 0; i < AB_PER_WAVE; ++i)
-            if (adst[i] >= 0) lds_load16(asrc[i] + (size_t)kt * A_ROW, &sA[buf][adst[i]]);
-        if (F8 && wave * 64 < BM) lds_load4(ascsrc + kt * 4, &sAsc[buf][wave * 64]);
-    };
-
-    uint4 bc[WN], bc2[WN], nc[WN], nc2[WN];
-    uint32_t bs[WN], ns[WN];
-    auto load_b = [&](int kt, uint4* c1, uint4* c2, uint32_t* sc) {
+            lds_load16(asrc[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
+        if (F8) lds_load4(ascsrc + kk * 4, (real && wave * 64 < BM) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
 #pragma unroll
         for (int s = 0; s < WN; ++s) {
-            const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kt;
+            const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
             if (F8) {
-                const uint4* q = reinterpret_cast<const uint4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
+                const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
                 c1[s] = q[0];
                 c2[s] = q[1];
                 sc[s] = p.b_scales[tile * kF8TileScale + lane];
             } else {
-                c1[s] = *reinterpret_cast<const uint4*>(p.b_codes + tile * kNvTileBytes + lane * 16);
+                c1[s] = *reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16);
                 sc[s] = *reinterpret_cast<const uint32_t*>(
                     p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
             }
@@ -224,18 +253,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int s = 0; s < WN; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue_a(0, 0);
-    load_b(0, bc, bc2, bs);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-            issue_a(kt + 1, buf ^ 1);
-            load_b(kt + 1, nc, nc2, ns);
-        }
+    auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
         if (F8) {
 #pragma unroll
             for (int ms = 0; ms < MS; ++ms) {
@@ -287,13 +305,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
                 }
             }
         }
-        if (more) {
+    };
+
+    u32x4 rc[P][WN], rc2[P][F8 ? WN : 1];
+    uint32_t rs[P][WN];
 #pragma unroll
-            for (int s = 0; s < WN; ++s) { bc[s] = nc[s]; bc2[s] = nc2[s]; bs[s] = ns[s]; }
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    for (int u = 0; u < P - 1; ++u) {
+        issue(u, u, rc[u], rc2[F8 ? u : 0], rs[u]);
+        asm volatile("" ::: "memory");  // keep each step's loads together, in step order
     }
+    // Step kt waits until only the loads of the P - 2 later steps are in
+    // flight, then refills the buffer freed by step kt - 1. Full groups of P
+    // steps run without branches between them, so every buffer keeps its
+    // registers across the loop; the remaining steps follow after it.
+    auto step = [&](int kt, int u) {
+        wait_vmcnt<L * (P - 2)>();
+        bare_barrier();
+#pragma unroll
+        for (int s = 0; s < WN; ++s) {
+            reg_fence(rc[u][s]);
+            reg_fence(rs[u][s]);
+            if (F8) reg_fence(rc2[F8 ? u : 0][s]);
+        }
+        const int nxt = (u + P - 1) % P;  // static once the loops are unrolled
+        issue(kt + P - 1, nxt, rc[nxt], rc2[F8 ? nxt : 0], rs[nxt]);
+        compute(u, rc[u], rc2[F8 ? u : 0], rs[u]);
+    };
+    int kt0 = 0;
+    for (; kt0 + P <= KT; kt0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) step(kt0 + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < P - 1; ++u)
+        if (kt0 + u < KT) step(kt0 + u, u);
+    wait_vmcnt<0>();
     gemm_epilogue<MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
 }
 
@@ -312,10 +358,10 @@ static void launch_wn(int bm_index, const GemmArgs& a, hipStream_t s, hipEvent_t
     const long long blocks = (long long)(a.N / (64 * WN)) * a.mt_max;
     const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(256);
     switch (bm_index) {
-        case 0: launch_timed(gemm_kernel<AB, 16, WN, EPI>, grid, block, s, t0, t1, a); break;
-        case 1: launch_timed(gemm_kernel<AB, 32, WN, EPI>, grid, block, s, t0, t1, a); break;
-        case 2: launch_timed(gemm_kernel<AB, 64, WN, EPI>, grid, block, s, t0, t1, a); break;
-        default: launch_timed(gemm_kernel<AB, 128, WN, EPI>, grid, block, s, t0, t1, a); break;
+        case 0: launch_timed(gemm_kernel<AB, 16, WN, EPI, 3>, grid, block, s, t0, t1, a); break;
+        case 1: launch_timed(gemm_kernel<AB, 32, WN, EPI, 3>, grid, block, s, t0, t1, a); break;
+        case 2: launch_timed(gemm_kernel<AB, 64, WN, EPI, 2>, grid, block, s, t0, t1, a); break;
+        default: launch_timed(gemm_kernel<AB, 128, WN, EPI, 2>, grid, block, s, t0, t1, a); break;
     }
 }
 
