@@ -34,6 +34,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t pack_pair(float lo, float hi, bool bf16) {
     if (bf16) return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
@@ -145,8 +146,8 @@ __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "m
 // register sets). Every wave issues the same number L of loads per step
 // (padding loads target a scratch LDS area), so "step kt has landed" is the
 // wait vmcnt <= L*(P-2) followed by a barrier.
-template <int AB, int BM, int WN, int EPI, int P>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
+template <int AB, int BM, int WN, int EPI, int P, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     constexpr bool F8 = AB == AB_FP8;
     constexpr bool BF = AB == AB_BF16_NV;
     constexpr int MS = BM / 16;
@@ -157,15 +158,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
     __shared__ int s_arow[BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
     // Block order: M-tile fastest (across experts), then N-block; consecutive
     // positions go to the same XCD (blocks are dealt round-robin over the 8
-    // XCDs and the grid is a multiple of 8), so concurrently running blocks of
-    // one XCD share an N-block's weight columns.
+    // XCDs and the grid is a multiple of 8). Each XCD then sweeps all M-tiles
+    // for its own N-blocks: the blocks it runs at a time share one N-block's
+    // weight columns in its L2, and the eight XCDs walk the A rows in step, so
+    // the shared last-level cache serves most A re-reads.
     const int total = gridDim.x;
     const int id = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
     const int mt = id % p.mt_max, nb = id / p.mt_max;
-    if (nb >= p.N / (64 * WN) || mt >= p.tiles[p.E]) return;
+    if (nb >= p.N / (16 * NW * WN) || mt >= p.tiles[p.E]) return;
     int lo = 0, hi = p.E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -175,38 +179,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
     const int mt_local = mt - p.tiles[e];
     const int row0 = p.offsets[e] + mt_local * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
-    for (int m = tid; m < BM; m += 256)
+    for (int m = tid; m < BM; m += NW * 64)
         s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
     __syncthreads();
 
     const int KT = p.Kdim / kTileK;
     const size_t tiles_e = (size_t)(p.N / kStrip) * KT;
-    const int gs0 = nb * (4 * WN) + wave * WN;  // first global strip of this wave
+    const int gs0 = nb * (NW * WN) + wave * WN;  // first global strip of this wave
     const uint8_t* abase = static_cast<const uint8_t*>(p.a);
     const size_t a_row_bytes = (size_t)p.Kdim * (F8 ? 1 : 2);
     const int r_any = s_arow[0];                 // rows past the group re-read a valid row
 
     // A staging: every 1 KB of the LDS tile is one wave-wide direct load in the
     // exact fragment order of the matrix-core operand.
-    //  f16/bf16: fragment block (ms, j) holds lane l' = row ms*16 + l'%16,
-    //            k = 32 j + 8 (l'/16) + [0, 8); wave w loads the blocks j = w.
-    //  fp8:      block (ms, h) holds lane l' = row ms*16 + l'%16,
-    //            k = 64 h + 16 (l'/16) + [0, 16); wave w loads blocks w + 4i.
-    constexpr int AB_PER_WAVE = F8 ? (MS * 2 + 3) / 4 : MS;
+    //  f16/bf16: block blk = 4 ms + j holds lane l' = row ms*16 + l'%16,
+    //            k = 32 j + 8 (l'/16) + [0, 8);
+    //  fp8:      block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
+    //            k = 64 h + 16 (l'/16) + [0, 16).
+    // Wave w loads the blocks w, w + NW, w + 2 NW, ...
+    constexpr int JB = F8 ? 2 : 4;
+    constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
     const uint8_t* asrc[AB_PER_WAVE];
     int adst[AB_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < AB_PER_WAVE; ++i) {
-        int ms, koff, blk;
-        if (F8) {
-            blk = wave + 4 * i;
-            ms = blk >> 1;
-            koff = (blk & 1) * 64 + 16 * (lane >> 4);
-        } else {
-            ms = i;
-            blk = ms * 4 + wave;
-            koff = (32 * wave + 8 * (lane >> 4)) * 2;
-        }
+        const int blk = wave + NW * i;
+        const int ms = blk / JB, j = blk % JB;
+        const int koff = F8 ? j * 64 + 16 * (lane >> 4) : (32 * j + 8 * (lane >> 4)) * 2;
         int r = r_any;
         if (ms < MS) {
             const int rr = s_arow[ms * 16 + (lane & 15)];
@@ -270,7 +269,43 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
                         av, bv, acc[ms][s], 0, 0, 0, asc, 0, (int)bs[s]);
                 }
             }
+        } else if (!BF) {
+            // fp16 operands: each E2M1 pair converts to two fp16 values, then
+            // one packed multiply by the block scale (E4M3, exact in fp16);
+            // code * scale has at most 6 significant bits and lies in
+            // [2^-10, 2688], so the product is exact.
+            h2 sfp[WN][2];
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                sfp[s][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, false);
+                sfp[s][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, true);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                u32x4 bq[WN];
+#pragma unroll
+                for (int s = 0; s < WN; ++s) {
+                    const uint32_t w = bc[s][j];
+                    const h2 f = (j & 1) ? sfp[s][j >> 1].yy : sfp[s][j >> 1].xx;
+                    const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * f;
+                    const h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * f;
+                    const h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * f;
+                    const h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * f;
+                    bq[s] = u32x4{__builtin_bit_cast(uint32_t, c0), __builtin_bit_cast(uint32_t, c1),
+                                  __builtin_bit_cast(uint32_t, c2), __builtin_bit_cast(uint32_t, c3)};
+                }
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
+#pragma unroll
+                    for (int s = 0; s < WN; ++s)
+                        acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
+                }
+            }
         } else {
+            // bf16 operands: code * scale in fp32 (exact), then the top half
+            // of each fp32 is the bf16 value (at most 6 significant bits).
             float sj[WN][4];
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
@@ -287,21 +322,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs p) {
                     float c[8];
                     e2m1x8_to_f32(w, c);
                     const float f = sj[s][j];
-                    bq[s] = make_uint4(pack_pair(c[0] * f, c[1] * f, BF), pack_pair(c[2] * f, c[3] * f, BF),
-                                       pack_pair(c[4] * f, c[5] * f, BF), pack_pair(c[6] * f, c[7] * f, BF));
+                    bq[s] = make_uint4(pack_pair(c[0] * f, c[1] * f, true), pack_pair(c[2] * f, c[3] * f, true),
+                                       pack_pair(c[4] * f, c[5] * f, true), pack_pair(c[6] * f, c[7] * f, true));
                 }
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
 #pragma unroll
-                    for (int s = 0; s < WN; ++s) {
-                        if (BF)
-                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq[s]), acc[ms][s], 0, 0, 0);
-                        else
-                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                                __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
-                    }
+                    for (int s = 0; s < WN; ++s)
+                        acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq[s]), acc[ms][s], 0, 0, 0);
                 }
             }
         }
@@ -353,25 +383,36 @@ static void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEven
     else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
 }
 
-template <int AB, int EPI, int WN>
-static void launch_wn(int bm_index, const GemmArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    const long long blocks = (long long)(a.N / (64 * WN)) * a.mt_max;
-    const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(256);
-    switch (bm_index) {
-        case 0: launch_timed(gemm_kernel<AB, 16, WN, EPI, 3>, grid, block, s, t0, t1, a); break;
-        case 1: launch_timed(gemm_kernel<AB, 32, WN, EPI, 3>, grid, block, s, t0, t1, a); break;
-        case 2: launch_timed(gemm_kernel<AB, 64, WN, EPI, 2>, grid, block, s, t0, t1, a); break;
-        default: launch_timed(gemm_kernel<AB, 128, WN, EPI, 2>, grid, block, s, t0, t1, a); break;
-    }
+template <int AB, int EPI, int BM, int WN, int P, int NW>
+static void launch_cfg(const GemmArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
+    const long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
+    const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(NW * 64);
+    launch_timed(gemm_kernel<AB, BM, WN, EPI, P, NW>, grid, block, s, t0, t1, a);
 }
 
 template <int AB, int EPI>
 static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s, hipEvent_t t0,
                             hipEvent_t t1) {
-    // four strips per wave (256 columns per block) for the wide M tiles, where
-    // each A fragment read from LDS then feeds four matrix-core operations
-    if (bm_index >= 2 && a.N % 256 == 0) launch_wn<AB, EPI, 4>(bm_index, a, s, t0, t1);
-    else launch_wn<AB, EPI, 2>(bm_index, a, s, t0, t1);
+    // Small M tiles (few rows per expert, weight streaming): three-stage
+    // pipeline, two strips per wave. Wide M tiles: four strips per wave, so
+    // each A fragment read from LDS feeds four matrix-core operations; with
+    // 512 columns per block, eight waves (two per SIMD) share one A tile,
+    // which halves the A re-reads against 256-column blocks.
+    constexpr int PW = AB == AB_FP8 ? 3 : 4;   // pipeline depth, four-wave wide tiles
+    constexpr int PW8 = AB == AB_FP8 ? 3 : 2;  // eight waves: what fits in 256 registers
+    switch (bm_index) {
+        case 0: launch_cfg<AB, EPI, 16, 2, 3, 4>(a, s, t0, t1); break;
+        case 1: launch_cfg<AB, EPI, 32, 2, 3, 4>(a, s, t0, t1); break;
+        case 2:
+            if (a.N % 256 == 0) launch_cfg<AB, EPI, 64, 4, 2, 4>(a, s, t0, t1);
+            else launch_cfg<AB, EPI, 64, 2, 2, 4>(a, s, t0, t1);
+            break;
+        default:
+            if (a.N % 256 != 0) launch_cfg<AB, EPI, 128, 2, 2, 4>(a, s, t0, t1);
+            else if (a.N % 512 == 0) launch_cfg<AB, EPI, 128, 4, PW8, 8>(a, s, t0, t1);
+            else launch_cfg<AB, EPI, 128, 4, PW, 4>(a, s, t0, t1);
+            break;
+    }
     return hipGetLastError();
 }
 
