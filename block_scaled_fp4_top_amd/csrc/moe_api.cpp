@@ -353,8 +353,14 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     g1.on_input = router_weight_on_input;
     g1.I = I;
     g1.topw = topw;
-    if (nv4 || f8) g1.out_f32 = WS(float, V_A2F);
-    else g1.out_bf16 = WS(uint16_t, V_A2F);
+    if (nv4) {
+        g1.out_f32 = WS(float, V_A2F);
+    } else if (f8) {
+        g1.a2_codes = WS(uint8_t, V_A2CODES);
+        g1.a2_scales = WS(uint8_t, V_A2SCALES);
+    } else {
+        g1.out_bf16 = WS(uint16_t, V_A2F);
+    }
     g1.amax_slot = mode == MOE_W4A4_TENSOR ? misc + kMiscA2Amax : nullptr;
     hipEvent_t t0, t1;
     timer_kernel_events(3, &t0, &t1);
@@ -364,10 +370,6 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
         HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, per_row ? QK_NV_ROW : QK_NV_TENSOR,
                                   misc + kMiscA2Amax, WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES),
                                   WS(float, V_A2G), WS(uint16_t, V_A2DEQ), stream),
-                "quantize FC2 input");
-    } else if (f8) {
-        HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, QK_MX, nullptr, WS(uint8_t, V_A2CODES),
-                                  WS(uint8_t, V_A2SCALES), nullptr, nullptr, stream),
                 "quantize FC2 input");
     }
 

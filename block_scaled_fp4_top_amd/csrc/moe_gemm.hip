@@ -41,6 +41,12 @@ __device__ __forceinline__ uint32_t pack_pair(float lo, float hi, bool bf16) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
+// SiLU(g) * u with the hardware exp2 and reciprocal (a few ulp in fp32).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 // Epilogue: acc[ms][s][i] holds C for row ms*16 + 4*(lane/16) + i of the
 // tile and column strip gs0 + s, lane % 16.
 template <int MS, int WN, int EPI>
@@ -49,6 +55,61 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                                               int lane) {
     const float gw = p.b_g ? p.b_g[e] : 1.0f;
     const int c16 = lane & 15;
+    if (EPI == EPI_FC1 && p.a2_codes) {
+        // MXFP8: the wave holds 32 consecutive FC2-input columns of each row
+        // per pair of output strips (lanes with equal lane/16 share a row), so
+        // it quantizes whole 32-element blocks: block max over the 16 lanes of
+        // the row group, E8M0 exponent, E4M3 codes. All lanes compute (rows
+        // past the group hold finite values of a re-read row); stores are
+        // guarded.
+        constexpr int OS = WN / 2;  // SwiGLU output strips; ReLU2 has WN
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = ms * 16 + 4 * (lane >> 4) + i;
+                const int row = row0 + min(m, rows - 1);
+                const float pw = p.on_input ? p.topw[p.row_to_route[row]] : 1.0f;
+                float a[WN];
+                int nout;
+                if (p.act == MOE_ACT_SWIGLU) {
+                    nout = OS;
+#pragma unroll
+                    for (int u = 0; u < OS; ++u) {
+                        a[u] = silu_mul(acc[ms][2 * u][i] * gw, acc[ms][2 * u + 1][i] * gw);
+                        if (p.on_input) a[u] = a[u] * pw;
+                    }
+                } else {
+                    nout = WN;
+#pragma unroll
+                    for (int u = 0; u < WN; ++u) {
+                        const float h = acc[ms][u][i] * gw;
+                        a[u] = h > 0.0f ? h * h : 0.0f;
+                        if (p.on_input) a[u] = a[u] * pw;
+                    }
+                }
+                const int col0 = (p.act == MOE_ACT_SWIGLU ? gs0 >> 1 : gs0) * 16;
+#pragma unroll
+                for (int b = 0; b < WN / 2; ++b) {
+                    if (2 * b + 1 >= nout) break;  // the host launches whole blocks only
+                    float ab = fmaxf(fabsf(a[2 * b]), fabsf(a[2 * b + 1]));
+#pragma unroll
+                    for (int off = 8; off >= 1; off >>= 1) ab = fmaxf(ab, __shfl_xor(ab, off));
+                    const int X = mxfp8_exponent(ab);
+                    const float inv = mxfp8_inv_scale(X);
+                    if (m < rows) {
+                        const size_t o = (size_t)(row0 + m) * p.I + col0 + 32 * b + c16;
+                        const uint32_t c = e4m3_code2(__fmul_rn(a[2 * b], inv), __fmul_rn(a[2 * b + 1], inv));
+                        p.a2_codes[o] = (uint8_t)c;
+                        p.a2_codes[o + 16] = (uint8_t)(c >> 8);
+                        if (c16 == 0)
+                            p.a2_scales[(size_t)(row0 + m) * (p.I / 32) + (col0 >> 5) + b] = (uint8_t)(X + 127);
+                    }
+                }
+            }
+        }
+        return;
+    }
     float amax = 0.0f;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -64,8 +125,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                 if (p.act == MOE_ACT_SWIGLU) {
 #pragma unroll
                     for (int u = 0; u < WN / 2; ++u) {
-                        const float hg = acc[ms][2 * u][i] * sc, hu = acc[ms][2 * u + 1][i] * sc;
-                        float a = hg / (1.0f + expf(-hg)) * hu;
+                        float a = silu_mul(acc[ms][2 * u][i] * sc, acc[ms][2 * u + 1][i] * sc);
                         if (p.on_input) a = a * pw;
                         const int col = ((gs0 + 2 * u) >> 1) * 16 + c16;
                         if (p.out_bf16) p.out_bf16[(size_t)row * p.I + col] = bf16_rne(a);
@@ -400,6 +460,17 @@ static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s, hipE
     // which halves the A re-reads against 256-column blocks.
     constexpr int PW = AB == AB_FP8 ? 3 : 4;   // pipeline depth, four-wave wide tiles
     constexpr int PW8 = AB == AB_FP8 ? 3 : 2;  // eight waves: what fits in 256 registers
+    // MXFP8 FC1 quantizes whole 32-column blocks in its epilogue: a wave must
+    // own 32 consecutive FC2-input columns, i.e. four strips under SwiGLU
+    // (2I is always a multiple of 256) and two under ReLU2.
+    constexpr bool QF = AB == AB_FP8 && EPI == EPI_FC1;
+    if constexpr (QF) {
+        if (bm_index <= 1 && a.N % 256 == 0) {
+            if (bm_index == 0) launch_cfg<AB, EPI, 16, 4, 3, 4>(a, s, t0, t1);
+            else launch_cfg<AB, EPI, 32, 4, 3, 4>(a, s, t0, t1);
+            return hipGetLastError();
+        }
+    }
     switch (bm_index) {
         case 0: launch_cfg<AB, EPI, 16, 2, 3, 4>(a, s, t0, t1); break;
         case 1: launch_cfg<AB, EPI, 32, 2, 3, 4>(a, s, t0, t1); break;

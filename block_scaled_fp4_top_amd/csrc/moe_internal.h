@@ -141,7 +141,7 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
     } else if (f8) {
         p->bytes[V_XCODES] = (size_t)T * H;
         p->bytes[V_XSCALES] = (size_t)T * H / 32;
-        p->bytes[V_A2F] = R * I * 4;
+        // the FC2 input is quantized in the FC1 epilogue: no fp32 copy
         p->bytes[V_A2CODES] = R * I;
         p->bytes[V_A2SCALES] = R * I / 32;
     } else {
@@ -201,6 +201,15 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
     uint32_t c = ((uint32_t)(e + 7) << 3) | keep;
     if (c > 0x7Eu) c = 0x7Eu;
     return s | c;
+}
+
+// Two E4M3 codes (x0 in bits 0..7, x1 in bits 8..15) by the hardware
+// converter, which rounds to nearest even; clamping to +-448 first gives the
+// saturating result of e4m3_code for every finite input.
+__device__ __forceinline__ uint32_t e4m3_code2(float x0, float x1) {
+    x0 = fminf(fmaxf(x0, -448.0f), 448.0f);
+    x1 = fminf(fmaxf(x1, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
 }
 
 // Value of a non-NaN E4M3 code.
@@ -270,15 +279,28 @@ __device__ __forceinline__ void nvfp4_block(const float* v, float g, uint32_t* p
 // MXFP8 quantization of one 32-element block (OCP MX v1.0 scale rule):
 // X = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an all-zero
 // block), elements E4M3(v * 2^-X). Returns the E8M0 code.
+// MXFP8 block exponent X from the block's max |v| (E8M0 code X + 127), and the
+// exact factor 2^-X that scales an element before its E4M3 rounding.
+__device__ __forceinline__ int mxfp8_exponent(float ab) {
+    const int X = ab == 0.0f ? -127 : floor_log2(ab) - 8;
+    return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+__device__ __forceinline__ float mxfp8_inv_scale(int X) {
+    return u2f((uint32_t)(127 - X) << 23);  // 2^-X, X <= 119 for finite input
+}
+
 __device__ __forceinline__ uint32_t mxfp8_block(const float* v, uint8_t* codes /*[32]*/) {
     float ab = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) ab = fmaxf(ab, fabsf(v[i]));
-    int X = ab == 0.0f ? -127 : floor_log2(ab) - 8;
-    X = X < -127 ? -127 : (X > 127 ? 127 : X);
-    const float inv = u2f((uint32_t)(127 - X) << 23);  // 2^-X, X <= 119 for finite input
+    const int X = mxfp8_exponent(ab);
+    const float inv = mxfp8_inv_scale(X);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) codes[i] = (uint8_t)e4m3_code(__fmul_rn(v[i], inv));
+    for (int i = 0; i < 32; i += 2) {
+        const uint32_t c = e4m3_code2(__fmul_rn(v[i], inv), __fmul_rn(v[i + 1], inv));
+        codes[i] = (uint8_t)c;
+        codes[i + 1] = (uint8_t)(c >> 8);
+    }
     return (uint32_t)(X + 127);
 }
 

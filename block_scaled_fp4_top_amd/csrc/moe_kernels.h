@@ -65,9 +65,11 @@ struct GemmArgs {
     // epilogue
     int act, on_input, I;
     const float* topw;
-    float* out_f32;      // FC1: fp32 [R][I] (quantized modes); FC2: O [R][N]
+    float* out_f32;      // FC1 NVFP4: fp32 [R][I] before quantization; FC2: O [R][N]
     uint16_t* out_bf16;  // FC1 W4A16: bf16 [R][I]
-    uint32_t* amax_slot; // FC1: amax of the FC2 input (quantized modes)
+    uint8_t* a2_codes;   // FC1 MXFP8: FC2-input E4M3 codes [R][I], quantized here
+    uint8_t* a2_scales;  //            and their E8M0 block scales [R][I/32]
+    uint32_t* amax_slot; // FC1: amax of the FC2 input (NVFP4 per-tensor)
     float* yacc;         // FC2 fused: [T][N]
     int fused;
 };

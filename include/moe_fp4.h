@@ -103,9 +103,11 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t 
  *   act must equal d->act. router_weight_on_input: 0 = output side (finalize
  *   weights p), 1 = input side (p applied to the FP32 activation output before
  *   the FC2-input quantization or bf16 store; finalize weights 1).
- *   deterministic_finalize: 1 = fixed-order unpermute+reduce (bit-identical run
- *   to run), 0 = fused scatter-add in the FC2 epilogue (fp32 atomics; the
- *   summation order, hence the last bits, may vary run to run).
+ *   deterministic_finalize: 1 = FC2 stores the permuted output O in fp32, then
+ *   a fixed-order unpermute+reduce in fp32 (bit-identical run to run);
+ *   0 = fused scatter-add in the FC2 epilogue (fp32 atomics; the summation
+ *   order, hence the last bits, may vary run to run).
+ *   MXFP8 quantizes the FC2 input in the FC1 epilogue (no fp32 copy).
  *   workspace: >= moe_workspace_bytes(d, T, K, mode) bytes, 256-byte aligned;
  *   afterwards it holds the intermediate views listed by moe_workspace_view.
  *   y: [T][H] bf16 bit patterns (output). */
@@ -140,7 +142,7 @@ int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8
  *   2 counts [E] i32             3 offsets [E+1] i32
  *   4 row_to_route [R] i32       5 route_to_row [R] i32
  *   6 x codes                    7 x scales               8 x global scale(s) f32
- *   9 FC2 input, fp32 before quantization [R][I] (W4A4, MXFP8) or bf16 (W4A16)
+ *   9 FC2 input, fp32 before quantization [R][I] (W4A4) or bf16 (W4A16)
  *   10 FC2-input codes           11 FC2-input scales      12 FC2-input global scale(s)
  *   13 permuted FC2 output O [R][H] f32 (deterministic finalize)
  * Returns MOE_ERR_INVALID for a view the mode does not produce. */

@@ -211,6 +211,58 @@ def check_prequant(a_gpu_perm: np.ndarray, ref: dict, mode: str, what=""):
         f"(worst |diff|/rowmax = {float((np.abs(a_g - a_ref) / scale).max()):.3e})"
 
 
+def check_a2_mxfp8(codes_perm: np.ndarray, scales_perm: np.ndarray, ref: dict, what=""):
+    """MXFP8 FC2 input quantized in the FC1 epilogue (no pre-quantization copy
+    exists). codes_perm [R][I] E4M3, scales_perm [R][I/32] E8M0, permuted row
+    order. Against the oracle's FP32 value v of each element, with
+    eps = TAU * rowmax (the FC1 accumulation-order allowance):
+      - the block exponent is one the block max can take within +-eps:
+        floor(log2(amax)) - 8 for amax in [amax_ref - eps, amax_ref + eps];
+      - the decoded element lies within eps plus half an E4M3 step (at its
+        own magnitude and the block scale) of v, or is the saturated +-448
+        times the block scale where |v| + eps reaches the saturation range."""
+    routes = ref["a_routes"]
+    rows = ref["route_to_row"][routes]
+    a32 = ref["a"].astype(np.float32).astype(np.float64)
+    n, I = a32.shape
+    c = codes_perm[rows]
+    sc = scales_perm[rows]
+    deq = R.mxfp8_dequant(c, sc)
+    X = sc.astype(np.int64) - 127
+    eps = TAU["mxfp8"] * np.abs(ref["a"]).max(1, keepdims=True)
+    blk = np.abs(a32).reshape(n, I // 32, 32).max(2)
+    e_blk = eps.repeat(I // 32, 1)
+
+    def expo(a):
+        out = np.full(a.shape, -127, np.int64)
+        nz = a > 0
+        out[nz] = np.clip(np.floor(np.log2(a[nz])).astype(np.int64) - 8, -127, 127)
+        return out
+
+    lo, hi = expo(np.maximum(blk - e_blk, 0.0)), expo(blk + e_blk)
+    assert np.all((X >= lo) & (X <= hi)), f"{what}: MXFP8 block exponent outside the allowed range"
+    Xe = np.repeat(X, 32, axis=1).astype(np.float64)
+    g = np.abs(deq) * np.exp2(-Xe)
+    step = np.where(g >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(g, 2.0 ** -6))) - 3), 2.0 ** -9)
+    bound = eps + 0.5 * step * np.exp2(Xe)
+    err = np.abs(deq - a32)
+    sat = (np.abs(deq) == 448.0 * np.exp2(Xe)) & (np.abs(a32) + eps >= 448.0 * np.exp2(Xe))
+    bad = (err > bound) & ~sat
+    assert not bad.any(), \
+        f"{what}: {int(bad.sum())} MXFP8 FC2-input elements off the oracle's rounding cell"
+
+
+def check_fc2_input(moe, d, ws, T: int, K: int, mode: str, ref: dict, what=""):
+    """The FC2 input the GPU produced, against the oracle's FC1 + activation."""
+    I = d.I
+    if mode == "mxfp8":
+        codes = moe.workspace_view(d, ws, T, K, mode, "a2_codes").cpu().numpy().reshape(T * K, I)
+        scales = moe.workspace_view(d, ws, T, K, mode, "a2_scales").cpu().numpy().reshape(T * K, I // 32)
+        return check_a2_mxfp8(codes, scales, ref, what)
+    a_pre = moe.workspace_view(d, ws, T, K, mode, "a2_pre").float().cpu().numpy()
+    return check_prequant(a_pre.reshape(T * K, I), ref, mode, what)
+
+
 def _requant_row(a32: np.ndarray, mode: str, g_tensor):
     """Dequantized FC2 input of one route row, as the oracle quantizes it."""
     from oracle import reference as Rr

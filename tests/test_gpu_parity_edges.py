@@ -14,7 +14,7 @@ if not torch.cuda.is_available():
 
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 from tests.helpers import (Inputs, assert_output_close, assert_output_close_flips,  # noqa: E402
-                           bf16_to_f64, check_prequant)
+                           bf16_to_f64, check_fc2_input)
 from tests.test_gpu_parity_small import check_routing, check_x_quant, run_layer  # noqa: E402
 
 
@@ -35,8 +35,7 @@ def _run_and_check(inp, K, mode, on_input, det=True, what=""):
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, inp.T, K, mode, ref)
     check_x_quant(d, ws, inp.T, K, mode, ref)
-    a_pre = moe.workspace_view(d, ws, inp.T, K, mode, "a2_pre").float().cpu().numpy()
-    check_prequant(a_pre.reshape(inp.T * K, inp.I), ref, mode, what)
+    check_fc2_input(moe, d, ws, inp.T, K, mode, ref, what)
     return assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what)
 
 

@@ -13,7 +13,7 @@ if not torch.cuda.is_available():  # collected on CPU runs too; every test is ma
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 from oracle import reference as R  # noqa: E402
 from tests.helpers import (Inputs, TOPW_REL, assert_output_close,  # noqa: E402
-                           assert_output_close_flips, bf16_to_f64, check_prequant,
+                           assert_output_close_flips, bf16_to_f64, check_fc2_input,
                            unpack_expert, unpack_nibbles)
 
 MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
@@ -80,8 +80,7 @@ def test_tiny_layer(mode, act, on_input, det):
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, T, K, mode, ref)
     check_x_quant(d, ws, T, K, mode, ref)
-    a_pre = moe.workspace_view(d, ws, T, K, mode, "a2_pre").float().cpu().numpy()
-    check_prequant(a_pre.reshape(T * K, I), ref, mode, f"{mode}/{act}")
+    check_fc2_input(moe, d, ws, T, K, mode, ref, f"{mode}/{act}")
     assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input,
                               f"{mode}/{act}/{on_input}/{det}")
 

@@ -20,7 +20,7 @@ import block_scaled_fp4_top_amd as moe  # noqa: E402
 from oracle import reference as R  # noqa: E402
 from synth_inputs import WORKLOADS  # noqa: E402
 from tests.helpers import (Inputs, assert_output_close_flips, bf16_to_f64,  # noqa: E402
-                           check_prequant, unpack_expert)
+                           check_fc2_input, unpack_expert)
 from tests.test_gpu_parity_small import check_routing, check_x_quant  # noqa: E402
 
 THREADS = 16
@@ -66,8 +66,7 @@ def test_workload_full_size(name):
         assert np.array_equal(w2c, oc2) and np.array_equal(w2s, os2), e
         if wl.wfmt == "nvfp4":
             assert g1 == og1 and g2 == og2
-    a_pre = moe.workspace_view(d, ws, wl.T, wl.K, wl.mode, "a2_pre").float().cpu().numpy()
-    check_prequant(a_pre.reshape(wl.R, wl.I), ref, wl.mode, name)
+    check_fc2_input(moe, d, ws, wl.T, wl.K, wl.mode, ref, name)
     toks = ref["tokens"]
     for fin, y in ys.items():
         yg = bf16_to_f64(y)[toks]
