@@ -23,6 +23,8 @@
 //    the token accumulator (fused finalize).
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "moe_kernels.h"
 
@@ -49,13 +51,23 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // Epilogue: acc[ms][s][i] holds C for row ms*16 + 4*(lane/16) + i of the
 // tile and column strip gs0 + s, lane % 16.
-template <int MS, int WN, int EPI>
+// Max over the 16 lanes of each DPP row (lanes with equal lane/16), by
+// rotations within the row: every lane ends with the row's max.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+    return v;
+}
+
+template <int AB, int MS, int WN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS][WN], int e,
                                               int row0, int rows, const int* s_arow, int gs0,
                                               int lane) {
     const float gw = p.b_g ? p.b_g[e] : 1.0f;
     const int c16 = lane & 15;
-    if (EPI == EPI_FC1 && p.a2_codes) {
+    if constexpr (EPI == EPI_FC1 && AB == AB_FP8) {
         // MXFP8: the wave holds 32 consecutive FC2-input columns of each row
         // per pair of output strips (lanes with equal lane/16 share a row), so
         // it quantizes whole 32-element blocks: block max over the 16 lanes of
@@ -93,8 +105,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                 for (int b = 0; b < WN / 2; ++b) {
                     if (2 * b + 1 >= nout) break;  // the host launches whole blocks only
                     float ab = fmaxf(fabsf(a[2 * b]), fabsf(a[2 * b + 1]));
-#pragma unroll
-                    for (int off = 8; off >= 1; off >>= 1) ab = fmaxf(ab, __shfl_xor(ab, off));
+                    ab = row16_max(ab);
                     const int X = mxfp8_exponent(ab);
                     const float inv = mxfp8_inv_scale(X);
                     if (m < rows) {
@@ -108,8 +119,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                 }
             }
         }
-        return;
-    }
+    } else {
     float amax = 0.0f;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
@@ -165,6 +175,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
         for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
         if (lane == 0) atomicMax(p.amax_slot, f2u(amax));
     }
+    }
 }
 
 // Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
@@ -209,8 +220,6 @@ __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "m
 template <int AB, int BM, int WN, int EPI, int P, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     constexpr bool F8 = AB == AB_FP8;
-    constexpr bool BF = AB == AB_BF16_NV;
-    constexpr int MS = BM / 16;
     constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
     constexpr int A_TILE = BM * A_ROW;
     __shared__ __attribute__((aligned(1024))) uint8_t sA[P][A_TILE];
@@ -243,194 +252,211 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
     __syncthreads();
 
-    const int KT = p.Kdim / kTileK;
-    const size_t tiles_e = (size_t)(p.N / kStrip) * KT;
-    const int gs0 = nb * (NW * WN) + wave * WN;  // first global strip of this wave
-    const uint8_t* abase = static_cast<const uint8_t*>(p.a);
-    const size_t a_row_bytes = (size_t)p.Kdim * (F8 ? 1 : 2);
-    const int r_any = s_arow[0];                 // rows past the group re-read a valid row
+    // Main loop and epilogue of one tile whose rows fit in MS 16-row groups
+    // (MS <= the kernel's BM / 16): the launch picks the smallest MS that covers
+    // the tile, so an expert's last, partly filled tile runs fewer matrix-core
+    // operations and loads.
+    auto body = [&](auto ms_tag) {
+        constexpr int MS = decltype(ms_tag)::value;
+        constexpr bool BF = AB == AB_BF16_NV;
+        constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
+        const int KT = p.Kdim / kTileK;
+        const size_t tiles_e = (size_t)(p.N / kStrip) * KT;
+        const int gs0 = nb * (NW * WN) + wave * WN;  // first global strip of this wave
+        const uint8_t* abase = static_cast<const uint8_t*>(p.a);
+        const size_t a_row_bytes = (size_t)p.Kdim * (F8 ? 1 : 2);
+        const int r_any = s_arow[0];                 // rows past the group re-read a valid row
 
-    // A staging: every 1 KB of the LDS tile is one wave-wide direct load in the
-    // exact fragment order of the matrix-core operand.
-    //  f16/bf16: block blk = 4 ms + j holds lane l' = row ms*16 + l'%16,
-    //            k = 32 j + 8 (l'/16) + [0, 8);
-    //  fp8:      block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
-    //            k = 64 h + 16 (l'/16) + [0, 16).
-    // Wave w loads the blocks w, w + NW, w + 2 NW, ...
-    constexpr int JB = F8 ? 2 : 4;
-    constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
-    const uint8_t* asrc[AB_PER_WAVE];
-    int adst[AB_PER_WAVE];
+        // A staging: every 1 KB of the LDS tile is one wave-wide direct load in the
+        // exact fragment order of the matrix-core operand.
+        //  f16/bf16: block blk = 4 ms + j holds lane l' = row ms*16 + l'%16,
+        //            k = 32 j + 8 (l'/16) + [0, 8);
+        //  fp8:      block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
+        //            k = 64 h + 16 (l'/16) + [0, 16).
+        // Wave w loads the blocks w, w + NW, w + 2 NW, ...
+        constexpr int JB = F8 ? 2 : 4;
+        constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
+        const uint8_t* asrc[AB_PER_WAVE];
+        int adst[AB_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < AB_PER_WAVE; ++i) {
-        const int blk = wave + NW * i;
-        const int ms = blk / JB, j = blk % JB;
-        const int koff = F8 ? j * 64 + 16 * (lane >> 4) : (32 * j + 8 * (lane >> 4)) * 2;
-        int r = r_any;
-        if (ms < MS) {
-            const int rr = s_arow[ms * 16 + (lane & 15)];
-            r = rr >= 0 ? rr : r_any;
-        }
-        asrc[i] = abase + (size_t)r * a_row_bytes + koff;
-        adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
-    }
-    const uint8_t* ascsrc = nullptr;
-    if (F8) {
-        const int m = wave * 64 + lane;
-        const int rr = m < BM ? s_arow[m] : -1;
-        ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
-    }
-    constexpr int L = AB_PER_WAVE + (F8 ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
-
-    // one step's loads; ks >= KT issues the same number of loads as padding
-    auto issue = [&](int ks, int buf, u32x4* c1, u32x4* c2, uint32_t* sc) {
-        const bool real = ks < KT;
-        const int kk = real ? ks : KT - 1;
-#pragma unroll
-        for (int i = 0; i < AB_PER_WAVE; ++i)
-            lds_load16(asrc[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
-        if (F8) lds_load4(ascsrc + kk * 4, (real && wave * 64 < BM) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
-#pragma unroll
-        for (int s = 0; s < WN; ++s) {
-            const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
-            if (F8) {
-                const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
-                c1[s] = q[0];
-                c2[s] = q[1];
-                sc[s] = p.b_scales[tile * kF8TileScale + lane];
-            } else {
-                c1[s] = *reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16);
-                sc[s] = *reinterpret_cast<const uint32_t*>(
-                    p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
+        for (int i = 0; i < AB_PER_WAVE; ++i) {
+            const int blk = wave + NW * i;
+            const int ms = blk / JB, j = blk % JB;
+            const int koff = F8 ? j * 64 + 16 * (lane >> 4) : (32 * j + 8 * (lane >> 4)) * 2;
+            int r = r_any;
+            if (ms < MS) {
+                const int rr = s_arow[ms * 16 + (lane & 15)];
+                r = rr >= 0 ? rr : r_any;
             }
+            asrc[i] = abase + (size_t)r * a_row_bytes + koff;
+            adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
         }
-    };
-
-    f32x4 acc[MS][WN];
-#pragma unroll
-    for (int ms = 0; ms < MS; ++ms)
-#pragma unroll
-        for (int s = 0; s < WN; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
+        const uint8_t* ascsrc = nullptr;
         if (F8) {
-#pragma unroll
-            for (int ms = 0; ms < MS; ++ms) {
-                const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + lane * 16]);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + 1024 + lane * 16]);
-                const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                                  (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
-#pragma unroll
-                for (int s = 0; s < WN; ++s) {
-                    const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w,
-                                      (int)bc2[s].x, (int)bc2[s].y, (int)bc2[s].z, (int)bc2[s].w};
-                    acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        av, bv, acc[ms][s], 0, 0, 0, asc, 0, (int)bs[s]);
-                }
-            }
-        } else if (!BF) {
-            // fp16 operands: each E2M1 pair converts to two fp16 values, then
-            // one packed multiply by the block scale (E4M3, exact in fp16);
-            // code * scale has at most 6 significant bits and lies in
-            // [2^-10, 2688], so the product is exact.
-            h2 sfp[WN][2];
-#pragma unroll
-            for (int s = 0; s < WN; ++s) {
-                sfp[s][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, false);
-                sfp[s][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, true);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x4 bq[WN];
-#pragma unroll
-                for (int s = 0; s < WN; ++s) {
-                    const uint32_t w = bc[s][j];
-                    const h2 f = (j & 1) ? sfp[s][j >> 1].yy : sfp[s][j >> 1].xx;
-                    const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * f;
-                    const h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * f;
-                    const h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * f;
-                    const h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * f;
-                    bq[s] = u32x4{__builtin_bit_cast(uint32_t, c0), __builtin_bit_cast(uint32_t, c1),
-                                  __builtin_bit_cast(uint32_t, c2), __builtin_bit_cast(uint32_t, c3)};
-                }
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
-#pragma unroll
-                    for (int s = 0; s < WN; ++s)
-                        acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
-                }
-            }
-        } else {
-            // bf16 operands: code * scale in fp32 (exact), then the top half
-            // of each fp32 is the bf16 value (at most 6 significant bits).
-            float sj[WN][4];
-#pragma unroll
-            for (int s = 0; s < WN; ++s) {
-                const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, false);
-                const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, true);
-                sj[s][0] = s01[0]; sj[s][1] = s01[1]; sj[s][2] = s23[0]; sj[s][3] = s23[1];
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint4 bq[WN];
-#pragma unroll
-                for (int s = 0; s < WN; ++s) {
-                    const uint32_t w = j == 0 ? bc[s].x : (j == 1 ? bc[s].y : (j == 2 ? bc[s].z : bc[s].w));
-                    float c[8];
-                    e2m1x8_to_f32(w, c);
-                    const float f = sj[s][j];
-                    bq[s] = make_uint4(pack_pair(c[0] * f, c[1] * f, true), pack_pair(c[2] * f, c[3] * f, true),
-                                       pack_pair(c[4] * f, c[5] * f, true), pack_pair(c[6] * f, c[7] * f, true));
-                }
-#pragma unroll
-                for (int ms = 0; ms < MS; ++ms) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
-#pragma unroll
-                    for (int s = 0; s < WN; ++s)
-                        acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq[s]), acc[ms][s], 0, 0, 0);
-                }
-            }
+            const int m = wave * 64 + lane;
+            const int rr = m < MS * 16 ? s_arow[m] : -1;
+            ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
         }
-    };
+        constexpr int L = AB_PER_WAVE + (F8 ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
 
-    u32x4 rc[P][WN], rc2[P][F8 ? WN : 1];
-    uint32_t rs[P][WN];
+        // one step's loads; ks >= KT issues the same number of loads as padding
+        auto issue = [&](int ks, int buf, u32x4* c1, u32x4* c2, uint32_t* sc) {
+            const bool real = ks < KT;
+            const int kk = real ? ks : KT - 1;
 #pragma unroll
-    for (int u = 0; u < P - 1; ++u) {
-        issue(u, u, rc[u], rc2[F8 ? u : 0], rs[u]);
-        asm volatile("" ::: "memory");  // keep each step's loads together, in step order
-    }
-    // Step kt waits until only the loads of the P - 2 later steps are in
-    // flight, then refills the buffer freed by step kt - 1. Full groups of P
-    // steps run without branches between them, so every buffer keeps its
-    // registers across the loop; the remaining steps follow after it.
-    auto step = [&](int kt, int u) {
-        wait_vmcnt<L * (P - 2)>();
-        bare_barrier();
+            for (int i = 0; i < AB_PER_WAVE; ++i)
+                lds_load16(asrc[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
+            if (F8) lds_load4(ascsrc + kk * 4, (real && wave * 64 < MS * 16) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
 #pragma unroll
-        for (int s = 0; s < WN; ++s) {
-            reg_fence(rc[u][s]);
-            reg_fence(rs[u][s]);
-            if (F8) reg_fence(rc2[F8 ? u : 0][s]);
+            for (int s = 0; s < WN; ++s) {
+                const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
+                if (F8) {
+                    const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
+                    c1[s] = q[0];
+                    c2[s] = q[1];
+                    sc[s] = p.b_scales[tile * kF8TileScale + lane];
+                } else {
+                    c1[s] = *reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16);
+                    sc[s] = *reinterpret_cast<const uint32_t*>(
+                        p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
+                }
+            }
+        };
+
+        f32x4 acc[MS][WN];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int s = 0; s < WN; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
+            if (F8) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + lane * 16]);
+                    const uint4 a1 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + 1024 + lane * 16]);
+                    const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w,
+                                          (int)bc2[s].x, (int)bc2[s].y, (int)bc2[s].z, (int)bc2[s].w};
+                        acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc[ms][s], 0, 0, 0, asc, 0, (int)bs[s]);
+                    }
+                }
+            } else if (!BF) {
+                // fp16 operands: each E2M1 pair converts to two fp16 values, then
+                // one packed multiply by the block scale (E4M3, exact in fp16);
+                // code * scale has at most 6 significant bits and lies in
+                // [2^-10, 2688], so the product is exact.
+                h2 sfp[WN][2];
+#pragma unroll
+                for (int s = 0; s < WN; ++s) {
+                    sfp[s][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, false);
+                    sfp[s][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, true);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x4 bq[WN];
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const uint32_t w = bc[s][j];
+                        const h2 f = (j & 1) ? sfp[s][j >> 1].yy : sfp[s][j >> 1].xx;
+                        const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * f;
+                        const h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * f;
+                        const h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * f;
+                        const h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * f;
+                        bq[s] = u32x4{__builtin_bit_cast(uint32_t, c0), __builtin_bit_cast(uint32_t, c1),
+                                      __builtin_bit_cast(uint32_t, c2), __builtin_bit_cast(uint32_t, c3)};
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
+#pragma unroll
+                        for (int s = 0; s < WN; ++s)
+                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
+                    }
+                }
+            } else {
+                // bf16 operands: code * scale in fp32 (exact), then the top half
+                // of each fp32 is the bf16 value (at most 6 significant bits).
+                float sj[WN][4];
+#pragma unroll
+                for (int s = 0; s < WN; ++s) {
+                    const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, false);
+                    const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, true);
+                    sj[s][0] = s01[0]; sj[s][1] = s01[1]; sj[s][2] = s23[0]; sj[s][3] = s23[1];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint4 bq[WN];
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const uint32_t w = j == 0 ? bc[s].x : (j == 1 ? bc[s].y : (j == 2 ? bc[s].z : bc[s].w));
+                        float c[8];
+                        e2m1x8_to_f32(w, c);
+                        const float f = sj[s][j];
+                        bq[s] = make_uint4(pack_pair(c[0] * f, c[1] * f, true), pack_pair(c[2] * f, c[3] * f, true),
+                                           pack_pair(c[4] * f, c[5] * f, true), pack_pair(c[6] * f, c[7] * f, true));
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
+#pragma unroll
+                        for (int s = 0; s < WN; ++s)
+                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq[s]), acc[ms][s], 0, 0, 0);
+                    }
+                }
+            }
+        };
+
+        u32x4 rc[P][WN], rc2[P][F8 ? WN : 1];
+        uint32_t rs[P][WN];
+#pragma unroll
+        for (int u = 0; u < P - 1; ++u) {
+            issue(u, u, rc[u], rc2[F8 ? u : 0], rs[u]);
+            asm volatile("" ::: "memory");  // keep each step's loads together, in step order
         }
-        const int nxt = (u + P - 1) % P;  // static once the loops are unrolled
-        issue(kt + P - 1, nxt, rc[nxt], rc2[F8 ? nxt : 0], rs[nxt]);
-        compute(u, rc[u], rc2[F8 ? u : 0], rs[u]);
+        // Step kt waits until only the loads of the P - 2 later steps are in
+        // flight, then refills the buffer freed by step kt - 1. Full groups of P
+        // steps run without branches between them, so every buffer keeps its
+        // registers across the loop; the remaining steps follow after it.
+        auto step = [&](int kt, int u) {
+            wait_vmcnt<L * (P - 2)>();
+            bare_barrier();
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                reg_fence(rc[u][s]);
+                reg_fence(rs[u][s]);
+                if (F8) reg_fence(rc2[F8 ? u : 0][s]);
+            }
+            const int nxt = (u + P - 1) % P;  // static once the loops are unrolled
+            issue(kt + P - 1, nxt, rc[nxt], rc2[F8 ? nxt : 0], rs[nxt]);
+            compute(u, rc[u], rc2[F8 ? u : 0], rs[u]);
+        };
+        int kt0 = 0;
+        for (; kt0 + P <= KT; kt0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) step(kt0 + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < P - 1; ++u)
+            if (kt0 + u < KT) step(kt0 + u, u);
+        wait_vmcnt<0>();
+        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
     };
-    int kt0 = 0;
-    for (; kt0 + P <= KT; kt0 += P) {
-#pragma unroll
-        for (int u = 0; u < P; ++u) step(kt0 + u, u);
+    if constexpr (BM >= 64) {
+        if (rows > BM / 2) body(std::integral_constant<int, BM / 16>{});
+        else if (BM == 128 && rows > 32) body(std::integral_constant<int, 4>{});
+        else if (rows > 16) body(std::integral_constant<int, 2>{});
+        else body(std::integral_constant<int, 1>{});
+    } else {
+        body(std::integral_constant<int, BM / 16>{});
     }
-#pragma unroll
-    for (int u = 0; u < P - 1; ++u)
-        if (kt0 + u < KT) step(kt0 + u, u);
-    wait_vmcnt<0>();
-    gemm_epilogue<MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
 }
 
 // ---- host launchers (device code above) ----
