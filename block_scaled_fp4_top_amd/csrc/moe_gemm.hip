@@ -276,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         // Wave w loads the blocks w, w + NW, w + 2 NW, ...
         constexpr int JB = F8 ? 2 : 4;
         constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
-        const uint8_t* asrc[AB_PER_WAVE];
+        uint32_t aoff[AB_PER_WAVE];  // byte offset of the lane's A row chunk (A < 4 GiB)
         int adst[AB_PER_WAVE];
 #pragma unroll
         for (int i = 0; i < AB_PER_WAVE; ++i) {
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                 const int rr = s_arow[ms * 16 + (lane & 15)];
                 r = rr >= 0 ? rr : r_any;
             }
-            asrc[i] = abase + (size_t)r * a_row_bytes + koff;
+            aoff[i] = (uint32_t)((size_t)r * a_row_bytes + koff);
             adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
         }
         const uint8_t* ascsrc = nullptr;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
             const int kk = real ? ks : KT - 1;
 #pragma unroll
             for (int i = 0; i < AB_PER_WAVE; ++i)
-                lds_load16(asrc[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
+                lds_load16(abase + aoff[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
             if (F8) lds_load4(ascsrc + kk * 4, (real && wave * 64 < MS * 16) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
@@ -379,6 +379,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                             acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                                 __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
                     }
+                    // keep each 32-deep slice's weights short-lived (no hoisting
+                    // of later slices' conversions, which spills at 256 registers)
+                    if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
                 // bf16 operands: code * scale in fp32 (exact), then the top half
@@ -506,7 +509,7 @@ static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s, hipE
             break;
         default:
             if (a.N % 256 != 0) launch_cfg<AB, EPI, 128, 2, 2, 4>(a, s, t0, t1);
-            else if (a.N % 512 == 0) launch_cfg<AB, EPI, 128, 4, PW8, 8>(a, s, t0, t1);
+            else if (AB != AB_BF16_NV && a.N % 512 == 0) launch_cfg<AB, EPI, 128, 4, PW8, 8>(a, s, t0, t1);
             else launch_cfg<AB, EPI, 128, 4, PW, 4>(a, s, t0, t1);
             break;
     }
