@@ -168,20 +168,30 @@ __global__ __launch_bounds__(256) void finalize_kernel(const void* __restrict__ 
     __syncthreads();
     for (int c = threadIdx.x * 4; c < H; c += 1024) {
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        for (int k = 0; k < K; ++k) {
-            const size_t off = (size_t)s_row[k] * H + c;
-            float o0, o1, o2, o3;
-            if (BF16) {
-                const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(O) + off);
-                o0 = u2f(q.x << 16); o1 = u2f(q.x & 0xFFFF0000u);
-                o2 = u2f(q.y << 16); o3 = u2f(q.y & 0xFFFF0000u);
-            } else {
-                const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + off);
-                o0 = q.x; o1 = q.y; o2 = q.z; o3 = q.w;
+        // the loads of up to 8 routes are issued together, then reduced in k order
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float4 q[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k0 + u < K) {
+                    const size_t off = (size_t)s_row[k0 + u] * H + c;
+                    if (BF16) {
+                        const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(O) + off);
+                        q[u] = make_float4(u2f(b.x << 16), u2f(b.x & 0xFFFF0000u), u2f(b.y << 16),
+                                           u2f(b.y & 0xFFFF0000u));
+                    } else {
+                        q[u] = *reinterpret_cast<const float4*>(static_cast<const float*>(O) + off);
+                    }
+                }
             }
-            const float wk = s_w[k];
-            a0 = __fmaf_rn(wk, o0, a0); a1 = __fmaf_rn(wk, o1, a1);
-            a2 = __fmaf_rn(wk, o2, a2); a3 = __fmaf_rn(wk, o3, a3);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k0 + u < K) {
+                    const float wk = s_w[k0 + u];
+                    a0 = __fmaf_rn(wk, q[u].x, a0); a1 = __fmaf_rn(wk, q[u].y, a1);
+                    a2 = __fmaf_rn(wk, q[u].z, a2); a3 = __fmaf_rn(wk, q[u].w, a3);
+                }
+            }
         }
         const uint32_t lo = (uint32_t)bf16_rne(a0) | ((uint32_t)bf16_rne(a1) << 16);
         const uint32_t hi = (uint32_t)bf16_rne(a2) | ((uint32_t)bf16_rne(a3) << 16);

@@ -87,21 +87,23 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < E; e += 256) bhist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// Exclusive scan over 1024 threads in LDS (Hillis-Steele, double buffered).
-__device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*[2][1024]*/) {
-    const int t = threadIdx.x;
-    int src = 0;
-    buf[t] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-        const int x = buf[src * 1024 + t] + (t >= off ? buf[src * 1024 + t - off] : 0);
-        buf[(1 - src) * 1024 + t] = x;
-        src = 1 - src;
-        __syncthreads();
+// Exclusive scan over the threads of a 1024-thread block: an inclusive scan
+// inside each wave by lane shuffles, then the preceding waves' totals from
+// LDS (two barriers in all).
+__device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*>= 16 ints*/) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int incl = buf[src * 1024 + t];
+    if (lane == 63) buf[w] = x;
     __syncthreads();
-    return incl - v;
+    int before = 0;
+    for (int i = 0; i < w; ++i) before += buf[i];
+    __syncthreads();  // buf may be reused by the next scan
+    return before + x - v;
 }
 
 // One block of 1024 threads (thread e = expert e): per-block bases by a
