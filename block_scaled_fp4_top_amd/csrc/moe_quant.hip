@@ -121,6 +121,53 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     }
 }
 
+// NVFP4 with one global scale per row, rows of at most 64 * 16 * NBL values:
+// one wave per row holds its row in registers (lane l owns the 16-element
+// blocks l, l + 64, ...), so the row max and the quantization read HBM once.
+template <bool BF16, int NBL>
+__global__ __launch_bounds__(256) void quant_rows_nvrow_kernel(const void* __restrict__ v, int rows,
+                                                               int cols,
+                                                               uint8_t* __restrict__ codes,
+                                                               uint8_t* __restrict__ scales,
+                                                               float* __restrict__ g,
+                                                               uint16_t* __restrict__ deq) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const size_t base = (size_t)row * cols;
+    const int nb = cols / 16;
+    float vv[NBL][16];
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+        const int b = lane + 64 * j;
+        if (b < nb) {
+            load16<BF16>(v, base + (size_t)b * 16, vv[j]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(vv[j][i]));
+        }
+    }
+    m = wave_max(m);
+    const float gg = __fdiv_rn(m, 2688.0f);
+    if (lane == 0) g[row] = gg;
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) {
+        const int b = lane + 64 * j;
+        if (b >= nb) break;
+        uint32_t packed[2], sf;
+        nvfp4_block(vv[j], gg, packed, &sf);
+        *reinterpret_cast<uint2*>(codes + base / 2 + (size_t)b * 8) = make_uint2(packed[0], packed[1]);
+        scales[(size_t)row * nb + b] = (uint8_t)sf;
+        if (deq) {
+            uint32_t h[8];
+            nvfp4_deq_f16(packed, sf, h);
+            uint4* dst = reinterpret_cast<uint4*>(deq + base + (size_t)b * 16);
+            dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+            dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+        }
+    }
+}
+
 // Max |v| over n elements into *slot (as fp32 bits; order-free atomicMax on
 // non-negative floats compared as unsigned integers).
 template <bool BF16>
@@ -328,6 +375,19 @@ hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, hip
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
                              const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
                              uint16_t* deq, hipStream_t s) {
+    if (kind == QK_NV_ROW && !(rows < 2048 && cols >= 1024) && cols <= 64 * 16 * 8) {
+        // single pass with the row in registers
+        const int nbl = (cols / 16 + 63) / 64;
+        const dim3 grid4((rows + 3) / 4), block4(256);
+#define QN(BF, N) hipLaunchKernelGGL((quant_rows_nvrow_kernel<BF, N>), grid4, block4, 0, s, v, rows, cols, codes, scales, g, deq)
+        if (in_bf16) {
+            if (nbl <= 1) QN(true, 1); else if (nbl <= 2) QN(true, 2); else if (nbl <= 4) QN(true, 4); else QN(true, 8);
+        } else {
+            if (nbl <= 1) QN(false, 1); else if (nbl <= 2) QN(false, 2); else if (nbl <= 4) QN(false, 4); else QN(false, 8);
+        }
+#undef QN
+        return hipGetLastError();
+    }
     const bool wide = rows < 2048 && cols >= 1024;  // few long rows: a block per row
     const dim3 grid(wide ? rows : (rows + 3) / 4), block(256);
 #define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, codes, scales, g, deq)

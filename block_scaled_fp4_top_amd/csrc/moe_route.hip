@@ -106,8 +106,9 @@ __device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*>= 16 
     return before + x - v;
 }
 
-// One block of 1024 threads (thread e = expert e): per-block bases by a
-// column scan over the block histograms, expert counts and offsets, and the
+// One block of 1024 threads: per-block bases by a column scan over the block
+// histograms (each expert's block list split among up to 1024 / E threads,
+// whose loads are issued eight at a time), expert counts and offsets, and the
 // exclusive scans of ceil(count / BM) that list the grouped-GEMM M-tiles.
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ bhist,
                                                          int nblk, int E, int R,
@@ -116,21 +117,57 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ tiles) {
     __shared__ int buf[2 * 1024];
-    const int e = threadIdx.x;
+    __shared__ int part[1024];  // [q][e]: sum, then exclusive prefix over q, of split q
+    __shared__ int s_off[kMaxE];
+    const int t = threadIdx.x;
+    int tpe = 1;
+    while (tpe * 2 * E <= 1024) tpe *= 2;
+    const int q = t / E, ec = t - q * E;
+    const bool active = q < tpe;
+    const int cb = (nblk + tpe - 1) / tpe;
+    const int b0 = min(nblk, q * cb), b1 = min(nblk, b0 + cb);
+    if (active) {
+        int sum = 0;
+        for (int b = b0; b < b1; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? bhist[(size_t)(b + u) * E + ec] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sum += v[u];
+        }
+        part[q * E + ec] = sum;
+    }
+    __syncthreads();
+    const int e = t;
     int run = 0;
     if (e < E) {
-        for (int b = 0; b < nblk; ++b) {
-            bbase[(size_t)b * E + e] = run;
-            run += bhist[(size_t)b * E + e];
+        for (int qq = 0; qq < tpe; ++qq) {
+            const int v = part[qq * E + e];
+            part[qq * E + e] = run;
+            run += v;
         }
     }
     const int off = block1024_exclusive_scan(e < E ? run : 0, buf);
     if (e < E) {
         counts[e] = run;
         offsets[e] = off;
-        for (int b = 0; b < nblk; ++b) bbase[(size_t)b * E + e] += off;
+        s_off[e] = off;
     }
     if (e == 0) offsets[E] = R;
+    __syncthreads();
+    if (active) {
+        int base = s_off[ec] + part[q * E + ec];
+        for (int b = b0; b < b1; b += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? bhist[(size_t)(b + u) * E + ec] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (b + u < b1) bbase[(size_t)(b + u) * E + ec] = base;
+                base += v[u];
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < kNumBM; ++i) {
         const int bm = bm_of(i);
