@@ -214,8 +214,17 @@ def main():
             graphs[i % copies].replay()
         torch.cuda.synchronize()
         dt_graph = time.perf_counter() - t0
+        # distribution: one event pair per replay (outside the timed loop above)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        evs[0].record()
+        for i in range(args.steps):
+            graphs[i % copies].replay()
+            evs[i + 1].record()
+        torch.cuda.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 5) for q in (10, 50, 90)}
         results[det] = (dt_graph / args.steps * 1e3, dt_eager / args.steps * 1e3,
-                        {k: v / max(nfw, 1) for k, v in st.items()})
+                        {k: v / max(nfw, 1) for k, v in st.items()}, pct)
         del graphs
 
     counts = moe.workspace_view(d, ws, wl.T, wl.K, wl.mode, "counts").cpu().numpy()
@@ -231,7 +240,7 @@ def main():
     bytes_fc2 = wb2 + fc2_in + fc2_out
     flops_fc1 = 2.0 * R_ * wl.N1 * wl.H
     flops_fc2 = 2.0 * R_ * wl.H * wl.I
-    ms_det, ms_eager, st_det = results[True] if True in results else results[False]
+    ms_det, ms_eager, st_det, pct_det = results[True] if True in results else results[False]
     kernel = "fc1" if st_det["fc1"] >= st_det["fc2"] else "fc2"
     kms = st_det[kernel]
     kbytes = bytes_fc1 if kernel == "fc1" else bytes_fc2
@@ -274,15 +283,17 @@ def main():
                    "timing": "hipGraph replay of one forward per step",
                    "weight_copies_rotated": copies, "touched_experts": touched},
         "eager_ms_per_step": round(ms_eager, 5),
+        "graph_step_ms_percentiles": pct_det,
         "stages_us": {k: round(v * 1e3, 2) for k, v in st_det.items()},
         "layer_tflops": round((flops_fc1 + flops_fc2) / (ms_det * 1e-3) / 1e12, 2),
         "layer_weight_gbs": round((wb1 + wb2) / (ms_det * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
     if False in results and True in results:
-        ms_f, ms_fe, st_f = results[False]
+        ms_f, ms_fe, st_f, pct_f = results[False]
         out["fused_finalize"] = {"value": round(wl.T / (ms_f * 1e-3), 1),
                                  "ms_per_step": round(ms_f, 5),
+                                 "graph_step_ms_percentiles": pct_f,
                                  "eager_ms_per_step": round(ms_fe, 5),
                                  "stages_us": {k: round(v * 1e3, 2) for k, v in st_f.items()}}
     out["cpu_baseline"] = None
