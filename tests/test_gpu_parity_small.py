@@ -162,7 +162,7 @@ def test_quantizer_zero_matrix():
     assert c[1, 5] == 8 and c.sum() == 8
 
 
-@pytest.mark.parametrize("mode", ["w4a4_token", "mxfp8", "w4a16"])
+@pytest.mark.parametrize("mode", MODES)
 def test_deterministic_repeat_and_graph_replay(mode):
     T, H, I, E, K = 24, 256, 128, 8, 3
     inp = Inputs(T, H, I, E, K, "swiglu", "normal")
@@ -197,6 +197,51 @@ def test_deterministic_repeat_and_graph_replay(mode):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y0)
+    # the graph reads its inputs at replay time: new x and logits, eager work
+    # in between, every replay against the eager result for the same inputs
+    inp2 = Inputs(T, H, I, E, K, "swiglu", "uniform", seed=5, make_weights=False)
+    x1, l1 = inp.x.clone(), inp.logits.clone()
+    y2 = moe.forward(d, blob, inp2.x, inp2.logits, K, mode, True, True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        src_x, src_l, ref = (inp2.x, inp2.logits, y2) if rep % 2 == 0 else (x1, l1, y0)
+        inp.x.copy_(src_x)
+        inp.logits.copy_(src_l)
+        y.fill_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"replay {rep}"
+
+
+@pytest.mark.parametrize("mode", ["w4a4_tensor", "mxfp8"])
+def test_fused_graph_replay(mode):
+    """Fused finalize under graph capture: the accumulator is cleared by a
+    kernel inside the graph on every replay."""
+    T, H, I, E, K = 24, 256, 128, 8, 3
+    inp = Inputs(T, H, I, E, K, "swiglu", "normal")
+    d = moe.Dims(E, H, I, "swiglu", _fmt(mode))
+    blob = moe.prepare_weights(d, inp.w1, inp.w2)
+    ws = torch.empty(moe.workspace_bytes(d, T, K, mode), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    yd = moe.forward(d, blob, inp.x, inp.logits, K, mode, False, True)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        moe.forward(d, blob, inp.x, inp.logits, K, mode, False, False, workspace=ws, out=y)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            moe.forward(d, blob, inp.x, inp.logits, K, mode, False, False, workspace=ws, out=y,
+                        stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_output_close(bf16_to_f64(y), bf16_to_f64(yd), f"fused graph replay {rep}")
 
 
 def test_fused_matches_deterministic():
