@@ -299,7 +299,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         }
         constexpr int L = AB_PER_WAVE + (F8 ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
 
-        // one step's loads; ks >= KT issues the same number of loads as padding
+        // Weight loads: small M tiles read each weight once, so they stream past
+    // the caches (non-temporal); wide tiles rely on L2 hits across the M-tiles
+    // of one expert and load normally.
+    auto load_b = [](const u32x4* q) -> u32x4 {
+        if constexpr (BM <= 32) return __builtin_nontemporal_load(q);
+        else return *q;
+    };
+    // one step's loads; ks >= KT issues the same number of loads as padding
         auto issue = [&](int ks, int buf, u32x4* c1, u32x4* c2, uint32_t* sc) {
             const bool real = ks < KT;
             const int kk = real ? ks : KT - 1;
@@ -312,11 +319,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                 const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
                 if (F8) {
                     const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
-                    c1[s] = q[0];
-                    c2[s] = q[1];
+                    c1[s] = load_b(q);
+                    c2[s] = load_b(q + 1);
                     sc[s] = p.b_scales[tile * kF8TileScale + lane];
                 } else {
-                    c1[s] = *reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16);
+                    c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16));
                     sc[s] = *reinterpret_cast<const uint32_t*>(
                         p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
                 }
