@@ -106,6 +106,23 @@ __device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*>= 16 
     return before + x - v;
 }
 
+// Three independent exclusive scans at once (same scheme, two barriers).
+__device__ __forceinline__ int3 block1024_exclusive_scan3(int3 v, int* buf /*>= 48 ints*/) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    int3 x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int a = __shfl_up(x.x, off), b = __shfl_up(x.y, off), c = __shfl_up(x.z, off);
+        if (lane >= off) { x.x += a; x.y += b; x.z += c; }
+    }
+    if (lane == 63) { buf[3 * w] = x.x; buf[3 * w + 1] = x.y; buf[3 * w + 2] = x.z; }
+    __syncthreads();
+    int3 before = make_int3(0, 0, 0);
+    for (int i = 0; i < w; ++i) { before.x += buf[3 * i]; before.y += buf[3 * i + 1]; before.z += buf[3 * i + 2]; }
+    __syncthreads();
+    return make_int3(before.x + x.x - v.x, before.y + x.y - v.y, before.z + x.z - v.z);
+}
+
 // One block of 1024 threads: per-block bases by a column scan over the block
 // histograms (each expert's block list split among up to 1024 / E threads,
 // whose loads are issued eight at a time), expert counts and offsets, and the
@@ -244,12 +261,31 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     __shared__ int32_t cnt[kSmallMaxE];
     __shared__ int32_t wh[16][kSmallMaxE];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    constexpr int kPer = kSmallMaxR / 1024;  // routes per thread, kept in registers
+    int xs[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int r = tid + 1024 * i;
+        xs[i] = r < R ? ids[r] : -1;
+    }
     for (int e = tid; e < kSmallMaxE; e += 1024) cnt[e] = 0;
     __syncthreads();
-    for (int r = tid; r < R; r += 1024) atomicAdd(&cnt[ids[r]], 1);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if (xs[i] >= 0) atomicAdd(&cnt[xs[i]], 1);
     __syncthreads();
     const int run = tid < E ? cnt[tid] : 0;
-    const int off = block1024_exclusive_scan(run, buf);
+    // expert offsets and the four tile-list offsets in one pass: all prefix
+    // sums stay below 2^16 here (R <= 16384, tiles <= R/16 + E), so two
+    // scans share each 32-bit word
+    int nt[kNumBM];
+#pragma unroll
+    for (int i = 0; i < kNumBM; ++i) nt[i] = tid < E ? (run + bm_of(i) - 1) / bm_of(i) : 0;
+    static_assert(kNumBM == 4, "packing below assumes four tile sizes");
+    const int3 pk = block1024_exclusive_scan3(
+        make_int3(run | (nt[0] << 16), nt[1] | (nt[2] << 16), nt[3]), buf);
+    const int off = pk.x & 0xFFFF;
+    const int toff[kNumBM] = {pk.x >> 16, pk.y & 0xFFFF, pk.y >> 16, pk.z};
     if (tid < E) {
         counts[tid] = run;
         offsets[tid] = off;
@@ -257,11 +293,8 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     if (tid == 0) offsets[E] = R;
 #pragma unroll
     for (int i = 0; i < kNumBM; ++i) {
-        const int bm = bm_of(i);
-        const int nt = tid < E ? (run + bm - 1) / bm : 0;
-        const int toff = block1024_exclusive_scan(nt, buf);
-        if (tid < E) tiles[i * (E + 1) + tid] = toff;
-        if (tid == E - 1) tiles[i * (E + 1) + E] = toff + nt;
+        if (tid < E) tiles[i * (E + 1) + tid] = toff[i];
+        if (tid == E - 1) tiles[i * (E + 1) + E] = toff[i] + nt[i];
     }
     if (tid < E) cnt[tid] = off;
     for (int e = tid; e < kSmallMaxE; e += 1024)
@@ -269,10 +302,13 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     __syncthreads();
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
-    for (int base = 0; base < R; base += 1024) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int base = 1024 * i;
+        if (base >= R) break;
         const int r = base + tid;
         const bool valid = r < R;
-        const int x = valid ? ids[r] : 0;
+        const int x = valid ? xs[i] : 0;
         uint64_t peers = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             const bool bit = (x >> b) & 1;
