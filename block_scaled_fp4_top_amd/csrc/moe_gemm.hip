@@ -1,26 +1,31 @@
 // S4/S6 grouped GEMMs with fused epilogues.
 //
 // C[r][n] = sum_k A[row(r)][k] * W_e[n][k] for the rows r of one expert e.
-// A block of 256 threads (4 waves) owns an M-tile of BM rows of one expert
-// (from the device tile list built by the permutation) and 4*WN strips of 16
-// output columns; wave w owns strips [w*WN, w*WN + WN).
-//  - A (activations) is staged through LDS per 128-wide K step, double
-//    buffered, in the exact order the matrix cores read it, so every wave's
-//    fragment read is 1 KB (f16/bf16) or 2 KB (fp8) of contiguous LDS.
+// A block of NW waves (4, or 8 for wide tiles) owns an M-tile of BM rows of
+// one expert (from the device tile list built by the permutation) and NW*WN
+// strips of 16 output columns; wave w owns strips [w*WN, w*WN + WN) and all
+// rows of the tile.
+//  - A (activations) is staged through LDS per 128-deep K step by direct
+//    global->LDS loads, in the exact order the matrix cores read it, so every
+//    wave's fragment read is 1 KB (f16/bf16) or 2 KB (fp8) of contiguous LDS.
 //  - B (weights) is read straight from HBM into registers: the prepared blob
 //    stores every 16 x 128 micro-tile as the register image of a 64-lane wave,
 //    so each load is a contiguous 1 KB (NVFP4) or 2 KB (MXFP8) per wave.
-//  - NVFP4: exact dequantization code * sf in registers (hardware fp4 -> f32
-//    convert at unit scale, one fp32 multiply by the E4M3 scale; the product
-//    has at most 6 significant bits so the f16/bf16 pack is exact), then
-//    v_mfma_f32_16x16x32_{f16,bf16}. The E4M3 block-16 scales do not fit the
-//    matrix cores' E8M0 block-32 scaling, so the scale is applied on the VALU.
+//  - P-stage software pipeline: the loads of the next P-1 steps are in flight
+//    while one step is multiplied (P LDS buffers for A, P register sets for B).
+//  - NVFP4: exact dequantization code * sf in registers (hardware fp4
+//    converter at unit scale, then the E4M3 block scale: a packed fp16 multiply
+//    for fp16 operands, an fp32 multiply for bf16; the product has at most 6
+//    significant bits, so it is exact), then v_mfma_f32_16x16x32_{f16,bf16}.
+//    The E4M3 block-16 scales do not fit the matrix cores' E8M0 block-32
+//    scaling, so the scale is applied on the VALU.
 //  - MXFP8: v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 block scales as
 //    the per-lane scale operands; no dequantization at all.
 //  - Epilogue: global scales (g_a * g_w), then FC1: SwiGLU/ReLU2, optional
-//    input-side router weight in FP32, store of the FC2 input (fp32 + amax, or
-//    bf16); FC2: store of the permuted output or fp32 atomic scatter-add into
-//    the token accumulator (fused finalize).
+//    input-side router weight in FP32, then the FC2 input: fp32 (+ amax) for
+//    NVFP4, bf16 for W4A16, or MXFP8 codes and scales quantized in place;
+//    FC2: store of the permuted output or fp32 atomic scatter-add into the
+//    token accumulator (fused finalize).
 #include <hip/hip_ext.h>
 
 #include <type_traits>
