@@ -123,6 +123,11 @@ static int check_mode(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
     if (T < 1) return fail(MOE_ERR_INVALID, "T=%d must be >= 1", T);
     if (K < 1 || K > d->E || K > kMaxK) return fail(MOE_ERR_INVALID, "K=%d outside [1, min(E=%d, %d)]", K, d->E, kMaxK);
     if ((long long)T * K > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*K=%lld too large", (long long)T * K);
+    // the GEMMs address their activation rows with 32-bit byte offsets
+    const long long widest = d->H > d->I ? d->H : d->I;
+    if ((long long)T * K * widest * 2 >= (1LL << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "T*K*max(H, I)*2 = %lld bytes of activations: 4 GiB or more",
+                    (long long)T * K * widest * 2);
     const bool want_f8 = mode == MOE_MXFP8;
     if (want_f8 != (d->wfmt == MOE_FMT_MXFP8))
         return fail(MOE_ERR_INVALID, "mode %d needs a %s weight blob", mode, want_f8 ? "MXFP8" : "NVFP4");

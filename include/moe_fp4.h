@@ -99,7 +99,8 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t 
  *   prepared: blob from moe_prepare_weights with the same `d` (NVFP4 blob for
  *             modes 0..2, MXFP8 blob for mode 3).
  *   x:        [T][H] bf16 bit patterns.            logits: [T][E] fp32 (finite).
- *   T >= 1, 1 <= K <= min(E, 64).
+ *   T >= 1, 1 <= K <= min(E, 64), T*K*max(H, I)*2 < 4 GiB (MOE_ERR_UNSUPPORTED
+ *   otherwise: the GEMMs address activation rows with 32-bit offsets).
  *   act must equal d->act. router_weight_on_input: 0 = output side (finalize
  *   weights p), 1 = input side (p applied to the FP32 activation output before
  *   the FC2-input quantization or bf16 store; finalize weights 1).

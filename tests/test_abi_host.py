@@ -82,6 +82,9 @@ def test_forward_rejects_before_launch(moe):
     assert _fwd(moe, d, wsb=1024) == 3                     # MOE_ERR_WORKSPACE
     assert "workspace" in moe._lib.moe_last_error().decode()
     assert _fwd(moe, _dims(moe, H=200)) == 2               # MOE_ERR_UNSUPPORTED
+    big = _dims(moe, E=64, H=8192, I=2048)
+    assert _fwd(moe, big, T=1 << 15, K=8) == 2              # activations of 4 GiB or more
+    assert "4 GiB" in moe._lib.moe_last_error().decode()
 
 
 def test_finalize_and_quantize_reject(moe):
