@@ -272,12 +272,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         const size_t a_row_bytes = (size_t)p.Kdim * (F8 ? 1 : 2);
         const int r_any = s_arow[0];                 // rows past the group re-read a valid row
 
-        // A staging: every 1 KB of the LDS tile is one wave-wide direct load in the
-        // exact fragment order of the matrix-core operand.
-        //  f16/bf16: block blk = 4 ms + j holds lane l' = row ms*16 + l'%16,
-        //            k = 32 j + 8 (l'/16) + [0, 8);
-        //  fp8:      block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
-        //            k = 64 h + 16 (l'/16) + [0, 16).
+        // A staging: every 1 KB of the LDS tile is one wave-wide direct load
+        // (lane l lands at byte 16 l).
+        //  f16/bf16: block blk = 4 ms + 2 h + g holds rows ms*16 + 8 g + [0, 8),
+        //    bytes 128 h + [0, 128) of the 256-byte K step: each row's request is
+        //    one full 128-byte line. Row r (0..15 in its group) puts its 16-byte
+        //    chunk c at slot (r % 8) * 8 + (c ^ (r % 8) ^ (r / 8)), so the
+        //    matrix-core reads (16 rows, one chunk each) hit distinct banks.
+        //  fp8: block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
+        //    k = 64 h + 16 (l'/16) + [0, 16), the operand's own fragment order
+        //    (measured faster for fp8 than the 128-byte-row form).
         // Wave w loads the blocks w, w + NW, w + 2 NW, ...
         constexpr int JB = F8 ? 2 : 4;
         constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
@@ -286,11 +290,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int i = 0; i < AB_PER_WAVE; ++i) {
             const int blk = wave + NW * i;
-            const int ms = blk / JB, j = blk % JB;
-            const int koff = F8 ? j * 64 + 16 * (lane >> 4) : (32 * j + 8 * (lane >> 4)) * 2;
+            const int ms = blk / JB, g = blk & 1, h = (blk % JB) >> 1;
+            const int r8 = lane >> 3;  // row within the 8-row half
+            const int koff = F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ g) << 4);
             int r = r_any;
             if (ms < MS) {
-                const int rr = s_arow[ms * 16 + (lane & 15)];
+                const int rr = s_arow[ms * 16 + (F8 ? (lane & 15) : 8 * g + r8)];
                 r = rr >= 0 ? rr : r_any;
             }
             aoff[i] = (uint32_t)((size_t)r * a_row_bytes + koff);
@@ -341,6 +346,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int s = 0; s < WN; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+        // f16/bf16: this lane's operand chunk in the staged A tile: row lane % 16,
+        // chunk lane / 16 (+ 4 for the second 64 bytes of a 128-byte half).
+        const int a_r7 = lane & 7, a_g = (lane >> 3) & 1;
+        const int a_slot0 = a_g * 1024 + a_r7 * 128 + ((((lane >> 4) ^ a_r7 ^ a_g)) << 4);
+        const int a_slot1 = a_slot0 ^ 64;
         auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
             if (F8) {
 #pragma unroll
@@ -385,7 +395,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     }
 #pragma unroll
                     for (int ms = 0; ms < MS; ++ms) {
-                        const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            &sA[buf][(ms * 4 + (j >> 1) * 2) * 1024 + ((j & 1) ? a_slot1 : a_slot0)]);
 #pragma unroll
                         for (int s = 0; s < WN; ++s)
                             acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -419,7 +430,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     }
 #pragma unroll
                     for (int ms = 0; ms < MS; ++ms) {
-                        const uint4 a = *reinterpret_cast<const uint4*>(&sA[buf][((ms * 4 + j) * 64 + lane) * 16]);
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            &sA[buf][(ms * 4 + (j >> 1) * 2) * 1024 + ((j & 1) ? a_slot1 : a_slot0)]);
 #pragma unroll
                         for (int s = 0; s < WN; ++s)
                             acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
