@@ -277,11 +277,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         //  f16/bf16: block blk = 4 ms + 2 h + g holds rows ms*16 + 8 g + [0, 8),
         //    bytes 128 h + [0, 128) of the 256-byte K step: each row's request is
         //    one full 128-byte line. Row r (0..15 in its group) puts its 16-byte
-        //    chunk c at slot (r % 8) * 8 + (c ^ (r % 8) ^ (r / 8)), so the
-        //    matrix-core reads (16 rows, one chunk each) hit distinct banks.
+        //    chunk c at slot (r % 8) * 8 + (c ^ (r % 8) ^ 7 (r / 8)): the 64
+        //    addresses of one matrix-core operand read (16 rows, one chunk each)
+        //    then differ modulo 1 KB and, within every 8-lane group, modulo 128
+        //    bytes, which keeps the read free of bank conflicts (checked with the
+        //    LDS conflict counter; without the factor 7 the reads conflicted).
         //  fp8: block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
-        //    k = 64 h + 16 (l'/16) + [0, 16), the operand's own fragment order
-        //    (measured faster for fp8 than the 128-byte-row form).
+        //    k = 64 h + 16 (l'/16) + [0, 16), the operand's own order (the
+        //    128-byte-row form measured 3 % slower here).
         // Wave w loads the blocks w, w + NW, w + 2 NW, ...
         constexpr int JB = F8 ? 2 : 4;
         constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
             const int blk = wave + NW * i;
             const int ms = blk / JB, g = blk & 1, h = (blk % JB) >> 1;
             const int r8 = lane >> 3;  // row within the 8-row half
-            const int koff = F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ g) << 4);
+            const int koff = F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ (7 * g)) << 4);
             int r = r_any;
             if (ms < MS) {
                 const int rr = s_arow[ms * 16 + (F8 ? (lane & 15) : 8 * g + r8)];
@@ -349,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         // f16/bf16: this lane's operand chunk in the staged A tile: row lane % 16,
         // chunk lane / 16 (+ 4 for the second 64 bytes of a 128-byte half).
         const int a_r7 = lane & 7, a_g = (lane >> 3) & 1;
-        const int a_slot0 = a_g * 1024 + a_r7 * 128 + ((((lane >> 4) ^ a_r7 ^ a_g)) << 4);
+        const int a_slot0 = a_g * 1024 + a_r7 * 128 + (((lane >> 4) ^ a_r7 ^ (7 * a_g)) << 4);
         const int a_slot1 = a_slot0 ^ 64;
         auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
             if (F8) {
