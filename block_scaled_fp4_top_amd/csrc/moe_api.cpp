@@ -320,12 +320,12 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     timer_mark(2, stream);
     if (nv4) {
         if (!per_row) HIP_TRY(launch_amax(x, 1, (size_t)T * H, misc + kMiscXAmax, stream), "x amax");
-        HIP_TRY(launch_quant_rows(x, 1, T, H, per_row ? QK_NV_ROW : QK_NV_TENSOR, misc + kMiscXAmax,
+        HIP_TRY(launch_quant_rows(x, 1, T, H, per_row ? QK_NV_ROW : QK_NV_TENSOR, misc + kMiscXAmax, 1, 1,
                                   WS(uint8_t, V_XCODES), WS(uint8_t, V_XSCALES), WS(float, V_XG),
                                   WS(uint16_t, V_XDEQ), stream),
                 "quantize x");
     } else if (f8) {
-        HIP_TRY(launch_quant_rows(x, 1, T, H, QK_MX, nullptr, WS(uint8_t, V_XCODES),
+        HIP_TRY(launch_quant_rows(x, 1, T, H, QK_MX, nullptr, 0, 0, WS(uint8_t, V_XCODES),
                                   WS(uint8_t, V_XSCALES), nullptr, nullptr, stream),
                 "quantize x");
     }
@@ -373,7 +373,7 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
 
     if (nv4) {
         HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, per_row ? QK_NV_ROW : QK_NV_TENSOR,
-                                  misc + kMiscA2Amax, WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES),
+                                  misc + kMiscA2Amax, kAmaxSlots, kAmaxStride, WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES),
                                   WS(float, V_A2G), WS(uint16_t, V_A2DEQ), stream),
                 "quantize FC2 input");
     }
@@ -447,6 +447,6 @@ extern "C" int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t 
         HIP_TRY(launch_fill_u32(slot, 1, 0u, stream), "clear scratch");
         HIP_TRY(launch_amax(v, 0, (size_t)rows * cols, slot, stream), "amax");
     }
-    HIP_TRY(launch_quant_rows(v, 0, rows, cols, qk, slot, codes, scales, g, nullptr, stream), "quantize");
+    HIP_TRY(launch_quant_rows(v, 0, rows, cols, qk, slot, 1, 1, codes, scales, g, nullptr, stream), "quantize");
     return MOE_OK;
 }

@@ -178,7 +178,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
     if (EPI == EPI_FC1 && p.amax_slot) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-        if (lane == 0) atomicMax(p.amax_slot, f2u(amax));
+        const int slot = (blockIdx.x * 4 + (threadIdx.x >> 6)) % kAmaxSlots;
+        if (lane == 0) atomicMax(p.amax_slot + slot * kAmaxStride, f2u(amax));
     }
     }
 }

@@ -99,6 +99,14 @@ inline bool make_blob_layout(const moe_dims& d, BlobLayout* L) {
 // ---------------------------------------------------------------------------
 // Workspace
 // ---------------------------------------------------------------------------
+// misc region (u32 words), cleared by the routing kernel of every forward:
+// [0] x amax bits; from word kMiscA2Amax the FC2-input amax as kAmaxSlots
+// partial maxima, one per 128-byte line (kAmaxStride words apart). The FC1
+// waves spread their atomics over them (one shared word made the per-tensor
+// FC1 14 % slower from atomic contention); readers take the max.
+constexpr int kAmaxSlots = 32, kAmaxStride = 32;
+constexpr int kMiscXAmax = 0, kMiscA2Amax = 32, kMiscWords = kMiscA2Amax + kAmaxSlots * kAmaxStride;
+
 enum WsView {
     V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
@@ -127,7 +135,7 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
     p->bytes[V_RT2ROW] = R * 4;
     p->bytes[V_TILES] = (size_t)kNumBM * (E + 1) * 4;
     p->bytes[V_BHIST] = (size_t)p->nblk * E * 4 * 2;
-    p->bytes[V_MISC] = 256;
+    p->bytes[V_MISC] = kMiscWords * 4;
     if (nv4) {
         p->bytes[V_XCODES] = (size_t)T * H / 2;
         p->bytes[V_XSCALES] = (size_t)T * H / 16;
@@ -156,9 +164,6 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
     }
     p->total = off;
 }
-
-// misc region (u32 words): [0] x amax bits, [1] FC2-input amax bits
-constexpr int kMiscXAmax = 0, kMiscA2Amax = 1;
 
 // ---------------------------------------------------------------------------
 // Device codecs (written independently of any reference implementation)

@@ -17,14 +17,16 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* b
                           int32_t* bbase, int32_t* counts, int32_t* offsets, int32_t* tiles,
                           int32_t* r2r, int32_t* rt2row, hipStream_t s);
 
-// Row quantizers. kind: 0 NVFP4 one global scale (from the amax in *amax_slot),
-// 1 NVFP4 one global scale per row, 2 MXFP8. in_bf16: input rows are bf16
-// (else fp32). deq (NVFP4 only, may be null): fp16 [rows][cols] of code * sf.
+// Row quantizers. kind: 0 NVFP4 one global scale (from the amax: the largest
+// of amax_slots words amax_stride apart from amax_slot, each the bits of a
+// non-negative partial maximum), 1 NVFP4 one global scale per row, 2 MXFP8. in_bf16: input
+// rows are bf16 (else fp32). deq (NVFP4 only, may be null): fp16 [rows][cols]
+// of code * sf.
 enum QuantKind { QK_NV_TENSOR = 0, QK_NV_ROW = 1, QK_MX = 2 };
 hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* amax_slot, hipStream_t s);
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
-                             const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
-                             uint16_t* deq, hipStream_t s);
+                             const uint32_t* amax_slot, int amax_slots, int amax_stride, uint8_t* codes,
+                             uint8_t* scales, float* g, uint16_t* deq, hipStream_t s);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, hipStream_t s);

@@ -61,6 +61,7 @@ template <int KIND, bool BF16, int WPR>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ v, int rows,
                                                          int cols,
                                                          const uint32_t* __restrict__ amax_slot,
+                                                         int amax_slots, int amax_stride,
                                                          uint8_t* __restrict__ codes,
                                                          uint8_t* __restrict__ scales,
                                                          float* __restrict__ g,
@@ -88,7 +89,9 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     }
     float gg;
     if (KIND == QK_NV_TENSOR) {
-        gg = __fdiv_rn(u2f(*amax_slot), 2688.0f);
+        uint32_t am = 0;  // partial maxima of non-negative floats: the max of their bits
+        for (int i = 0; i < amax_slots; ++i) am = max(am, amax_slot[(size_t)i * amax_stride]);
+        gg = __fdiv_rn(u2f(am), 2688.0f);
         if (row == 0 && lt == 0) g[0] = gg;
     } else {
         float m = 0.0f;
@@ -373,8 +376,8 @@ hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, hip
 }
 
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
-                             const uint32_t* amax_slot, uint8_t* codes, uint8_t* scales, float* g,
-                             uint16_t* deq, hipStream_t s) {
+                             const uint32_t* amax_slot, int amax_slots, int amax_stride, uint8_t* codes,
+                             uint8_t* scales, float* g, uint16_t* deq, hipStream_t s) {
     if (kind == QK_NV_ROW && !(rows < 2048 && cols >= 1024) && cols <= 64 * 16 * 8) {
         // single pass with the row in registers
         const int nbl = (cols / 16 + 63) / 64;
@@ -390,7 +393,7 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
     }
     const bool wide = rows < 2048 && cols >= 1024;  // few long rows: a block per row
     const dim3 grid(wide ? rows : (rows + 3) / 4), block(256);
-#define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, codes, scales, g, deq)
+#define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, amax_slots, amax_stride, codes, scales, g, deq)
 #define QRW(KD, BF) do { if (wide) QR(KD, BF, 4); else QR(KD, BF, 1); } while (0)
     if (in_bf16) {
         if (kind == QK_NV_TENSOR) QRW(QK_NV_TENSOR, true);

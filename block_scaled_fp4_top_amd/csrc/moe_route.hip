@@ -99,7 +99,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                                                          int E, int K, int32_t* __restrict__ ids,
                                                          float* __restrict__ topw,
                                                          uint32_t* __restrict__ misc) {
-    if (blockIdx.x == 0 && threadIdx.x < 8) misc[threadIdx.x] = 0u;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < kMiscWords; i += blockDim.x) misc[i] = 0u;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
