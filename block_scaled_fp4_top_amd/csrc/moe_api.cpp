@@ -319,8 +319,10 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     }
     timer_mark(2, stream);
     if (nv4) {
-        if (!per_row) HIP_TRY(launch_amax(x, 1, (size_t)T * H, misc + kMiscXAmax, stream), "x amax");
-        HIP_TRY(launch_quant_rows(x, 1, T, H, per_row ? QK_NV_ROW : QK_NV_TENSOR, misc + kMiscXAmax, 1, 1,
+        if (!per_row)
+            HIP_TRY(launch_amax(x, 1, (size_t)T * H, misc + kMiscXAmax, kAmaxSlots, kAmaxStride, stream),
+                    "x amax");
+        HIP_TRY(launch_quant_rows(x, 1, T, H, per_row ? QK_NV_ROW : QK_NV_TENSOR, misc + kMiscXAmax, kAmaxSlots, kAmaxStride,
                                   WS(uint8_t, V_XCODES), WS(uint8_t, V_XSCALES), WS(float, V_XG),
                                   WS(uint16_t, V_XDEQ), stream),
                 "quantize x");
@@ -445,7 +447,7 @@ extern "C" int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t 
     const int qk = kind == 0 ? QK_NV_TENSOR : (kind == 1 ? QK_NV_ROW : QK_MX);
     if (qk == QK_NV_TENSOR) {
         HIP_TRY(launch_fill_u32(slot, 1, 0u, stream), "clear scratch");
-        HIP_TRY(launch_amax(v, 0, (size_t)rows * cols, slot, stream), "amax");
+        HIP_TRY(launch_amax(v, 0, (size_t)rows * cols, slot, 1, 1, stream), "amax");
     }
     HIP_TRY(launch_quant_rows(v, 0, rows, cols, qk, slot, 1, 1, codes, scales, g, nullptr, stream), "quantize");
     return MOE_OK;

@@ -100,12 +100,14 @@ inline bool make_blob_layout(const moe_dims& d, BlobLayout* L) {
 // Workspace
 // ---------------------------------------------------------------------------
 // misc region (u32 words), cleared by the routing kernel of every forward:
-// [0] x amax bits; from word kMiscA2Amax the FC2-input amax as kAmaxSlots
-// partial maxima, one per 128-byte line (kAmaxStride words apart). The FC1
-// waves spread their atomics over them (one shared word made the per-tensor
-// FC1 14 % slower from atomic contention); readers take the max.
+// the x amax and the FC2-input amax, each as kAmaxSlots partial maxima on
+// separate 128-byte lines (kAmaxStride words apart), from words kMiscXAmax
+// and kMiscA2Amax. Writers spread their atomics over the slots (one shared
+// word made the per-tensor decode FC1 14 % slower and the x amax pass 20 us
+// long from atomic contention); readers take the max.
 constexpr int kAmaxSlots = 32, kAmaxStride = 32;
-constexpr int kMiscXAmax = 0, kMiscA2Amax = 32, kMiscWords = kMiscA2Amax + kAmaxSlots * kAmaxStride;
+constexpr int kMiscXAmax = 0, kMiscA2Amax = kAmaxSlots * kAmaxStride;
+constexpr int kMiscWords = 2 * kAmaxSlots * kAmaxStride;
 
 enum WsView {
     V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,

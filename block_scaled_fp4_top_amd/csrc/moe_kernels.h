@@ -23,7 +23,9 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* b
 // rows are bf16 (else fp32). deq (NVFP4 only, may be null): fp16 [rows][cols]
 // of code * sf.
 enum QuantKind { QK_NV_TENSOR = 0, QK_NV_ROW = 1, QK_MX = 2 };
-hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* amax_slot, hipStream_t s);
+// Max |v| into the nslots words stride apart from amax_slot (already cleared).
+hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* amax_slot, int nslots,
+                       int stride, hipStream_t s);
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
                              const uint32_t* amax_slot, int amax_slots, int amax_stride, uint8_t* codes,
                              uint8_t* scales, float* g, uint16_t* deq, hipStream_t s);

@@ -89,9 +89,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     }
     float gg;
     if (KIND == QK_NV_TENSOR) {
-        uint32_t am = 0;  // partial maxima of non-negative floats: the max of their bits
-        for (int i = 0; i < amax_slots; ++i) am = max(am, amax_slot[(size_t)i * amax_stride]);
-        gg = __fdiv_rn(u2f(am), 2688.0f);
+        // the partial maxima (amax_slots <= 64), one per lane, then the wave's max
+        const int ln = tid & 63;
+        const float am = wave_max(ln < amax_slots ? u2f(amax_slot[(size_t)ln * amax_stride]) : 0.0f);
+        gg = __fdiv_rn(am, 2688.0f);
         if (row == 0 && lt == 0) g[0] = gg;
     } else {
         float m = 0.0f;
@@ -171,13 +172,23 @@ __global__ __launch_bounds__(256) void quant_rows_nvrow_kernel(const void* __res
     }
 }
 
-// Max |v| over n elements into *slot (as fp32 bits; order-free atomicMax on
-// non-negative floats compared as unsigned integers).
+// Max |v| over n elements as fp32 bits (order-free atomicMax on non-negative
+// floats compared as unsigned integers). Block b folds its maximum into word
+// (b % nslots) * stride of slot: spreading the atomics over words on separate
+// lines avoids the serialisation of many atomics on one address.
 template <bool BF16>
 __global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ v, size_t n,
-                                                   uint32_t* __restrict__ slot) {
+                                                   uint32_t* __restrict__ slot, int nslots,
+                                                   int stride) {
     float m = 0.0f;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    const size_t n16 = n / 16;  // 16-element chunks (v is 16-byte aligned)
+    for (size_t c = (size_t)blockIdx.x * 256 + threadIdx.x; c < n16; c += (size_t)gridDim.x * 256) {
+        float q[16];
+        load16<BF16>(v, c * 16, q);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(q[i]));
+    }
+    for (size_t i = n16 * 16 + (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
         m = fmaxf(m, fabsf(load1<BF16>(v, i)));
     m = wave_max(m);
     __shared__ float red[4];
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ v, s
     __syncthreads();
     if (threadIdx.x == 0) {
         m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        atomicMax(slot, f2u(m));
+        atomicMax(slot + (size_t)(blockIdx.x % nslots) * stride, f2u(m));
     }
 }
 
@@ -369,9 +380,11 @@ hipError_t launch_write_header(const BlobHeader& h, void* dst, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, hipStream_t s) {
-    if (in_bf16) hipLaunchKernelGGL(amax_kernel<true>, dim3(grid_for(n, 2048)), dim3(256), 0, s, v, n, slot);
-    else hipLaunchKernelGGL(amax_kernel<false>, dim3(grid_for(n, 2048)), dim3(256), 0, s, v, n, slot);
+hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, int nslots, int stride,
+                       hipStream_t s) {
+    const dim3 grid(grid_for((n + 15) / 16, 1024)), block(256);
+    if (in_bf16) hipLaunchKernelGGL(amax_kernel<true>, grid, block, 0, s, v, n, slot, nslots, stride);
+    else hipLaunchKernelGGL(amax_kernel<false>, grid, block, 0, s, v, n, slot, nslots, stride);
     return hipGetLastError();
 }
 
