@@ -6,8 +6,9 @@
 // strips of 16 output columns; wave w owns strips [w*WN, w*WN + WN) and all
 // rows of the tile.
 //  - A (activations) is staged through LDS per 128-deep K step by direct
-//    global->LDS loads, in the exact order the matrix cores read it, so every
-//    wave's fragment read is 1 KB (f16/bf16) or 2 KB (fp8) of contiguous LDS.
+//    global->LDS loads: f16/bf16 as 8 rows x one 128-byte line per load, in an
+//    XOR-swizzled layout whose operand reads are free of bank conflicts; fp8
+//    in the operand's own order (16 rows x 64 bytes per load).
 //  - B (weights) is read straight from HBM into registers: the prepared blob
 //    stores every 16 x 128 micro-tile as the register image of a 64-lane wave,
 //    so each load is a contiguous 1 KB (NVFP4) or 2 KB (MXFP8) per wave.
@@ -22,7 +23,8 @@
 //  - MXFP8: v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 block scales as
 //    the per-lane scale operands; no dequantization at all.
 //  - Epilogue: global scales (g_a * g_w), then FC1: SwiGLU/ReLU2, optional
-//    input-side router weight in FP32, then the FC2 input: fp32 (+ amax) for
+//    input-side router weight in FP32, then the FC2 input: fp32 (+ partial
+//    maxima of |value| for the per-tensor global scale) for
 //    NVFP4, bf16 for W4A16, or MXFP8 codes and scales quantized in place;
 //    FC2: store of the permuted output or fp32 atomic scatter-add into the
 //    token accumulator (fused finalize).
