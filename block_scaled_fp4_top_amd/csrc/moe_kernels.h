@@ -73,7 +73,7 @@ struct GemmArgs {
     uint16_t* out_bf16;  // FC1 W4A16: bf16 [R][I]
     uint8_t* a2_codes;   // FC1 MXFP8: FC2-input E4M3 codes [R][I], quantized here
     uint8_t* a2_scales;  //            and their E8M0 block scales [R][I/32]
-    uint32_t* amax_slot; // FC1: amax of the FC2 input (NVFP4 per-tensor)
+    uint32_t* amax_slot; // FC1: kAmaxSlots partial maxima of the FC2 input, kAmaxStride apart (NVFP4 per-tensor)
     float* yacc;         // FC2 fused: [T][N]
     int fused;
 };
