@@ -231,7 +231,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
     constexpr int A_TILE = BM * A_ROW;
     __shared__ __attribute__((aligned(1024))) uint8_t sA[P][A_TILE];
-    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][F8 ? BM : 1];
+    // A scales (fp8): one wave-wide 4-byte direct load per step writes 64
+    // words, so each buffer holds at least 64 rows' words even for BM < 64.
+    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][F8 ? (BM > 64 ? BM : 64) : 1];
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
     __shared__ int s_arow[BM];
 

@@ -1,0 +1,54 @@
+"""GPU parity over a seeded random sample of layer shapes and modes.
+
+Each case draws T, E, K, H, I, the activation, the mode, the placement of the
+router weight and the finalize variant from a fixed-seed generator, so the
+sample reaches the launch configurations the fixed cases may miss: every
+M-tile size (chosen from the mean rows per expert), weight column counts that
+are and are not multiples of 256 and 512, ragged expert groups and empty
+experts. Every case checks routing and permutation bit-exactly, the FC1-input
+and FC2-input quantization, and the output against the oracle's bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.helpers import Inputs, assert_output_close_flips, bf16_to_f64, check_fc2_input  # noqa: E402
+from tests.test_gpu_parity_small import check_routing, check_x_quant, run_layer  # noqa: E402
+import block_scaled_fp4_top_amd as moe  # noqa: E402
+
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
+
+
+def _cases(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 3, 8, 17, 40, 64]))
+        K = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 5, 33, 96, 200, 300]))
+        H = int(rng.choice([128, 256, 384, 640]))
+        I = int(rng.choice([128, 256, 384]))
+        act = str(rng.choice(["swiglu", "relu2"]))
+        mode = MODES[i % len(MODES)]
+        on_input = bool(rng.integers(0, 2))
+        det = bool(rng.integers(0, 4) != 0)  # mostly deterministic, some fused
+        out.append((i, T, H, I, E, K, act, mode, on_input, det))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"case{c[0]}")
+def test_random_shape(case):
+    i, T, H, I, E, K, act, mode, on_input, det = case
+    what = f"case{i} T={T} H={H} I={I} E={E} K={K} {act} {mode} on_input={on_input} det={det}"
+    print(what, flush=True)
+    inp = Inputs(T, H, I, E, K, act, "normal", seed=100 + i)
+    d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
+    check_routing(d, ws, T, K, mode, ref)
+    check_x_quant(d, ws, T, K, mode, ref)
+    check_fc2_input(moe, d, ws, T, K, mode, ref, what)
+    assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what)
