@@ -16,6 +16,11 @@ from synth_inputs.gen import STREAM_W1, STREAM_W2, make_weight
 MAX_ERR_RMS = 2e-2
 REL_FRO = 1e-2
 TOPW_REL = 1e-6
+# The output is bf16 by the interface: rounding even the exact result costs up
+# to BF16_U * |y| per element (unit roundoff 2^-8). On heavy-tailed outputs
+# that alone can exceed 2e-2 * rms (measured up to 2.5e-2 on shapes outside
+# the five workloads), so tests of arbitrary shapes bound the error beyond it.
+BF16_U = 2.0 ** -8
 
 
 def bits16(t: torch.Tensor) -> np.ndarray:
@@ -26,18 +31,23 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().float().numpy().astype(np.float64)
 
 
-def out_errors(y_gpu: np.ndarray, y_ref: np.ndarray):
+def out_errors(y_gpu: np.ndarray, y_ref: np.ndarray, round_allow=False):
+    """max|err|/rms and the relative Frobenius error; with round_allow the max
+    is taken over |err| - BF16_U * |y_ref| (the error beyond the output's own
+    bf16 rounding)."""
     err = y_gpu - y_ref
     rms = math.sqrt(float(np.mean(y_ref * y_ref)))
-    max_rel = float(np.max(np.abs(err))) / rms
+    e = np.abs(err) - BF16_U * np.abs(y_ref) if round_allow else np.abs(err)
+    max_rel = float(np.max(e)) / rms
     fro = float(np.linalg.norm(err) / np.linalg.norm(y_ref))
     return max_rel, fro
 
 
-def assert_output_close(y_gpu: np.ndarray, y_ref: np.ndarray, what=""):
-    max_rel, fro = out_errors(y_gpu, y_ref)
+def assert_output_close(y_gpu: np.ndarray, y_ref: np.ndarray, what="", round_allow=False):
+    max_rel, fro = out_errors(y_gpu, y_ref, round_allow)
+    beyond = " beyond bf16 rounding" if round_allow else ""
     assert max_rel <= MAX_ERR_RMS and fro <= REL_FRO, \
-        f"{what}: max|err|/rms={max_rel:.3e} (bar {MAX_ERR_RMS}), rel Frobenius={fro:.3e} (bar {REL_FRO})"
+        f"{what}: max|err|{beyond}/rms={max_rel:.3e} (bar {MAX_ERR_RMS}), rel Frobenius={fro:.3e} (bar {REL_FRO})"
     return max_rel, fro
 
 
@@ -284,7 +294,7 @@ def _requant_row(a32: np.ndarray, mode: str, g_tensor):
 
 
 def assert_output_close_flips(y_gpu: np.ndarray, ref: dict, W, mode: str, K: int,
-                              on_input: bool, what=""):
+                              on_input: bool, what="", round_allow=False):
     """The output bar, allowing FC2-input rounding decisions that are ambiguous.
 
     Where the oracle's pre-quantization value of an FC2-input element lies
@@ -295,7 +305,7 @@ def assert_output_close_flips(y_gpu: np.ndarray, ref: dict, W, mode: str, K: int
     alternative the GPU output is closest to; then the usual bar applies."""
     y_ref = ref["y"]
     try:
-        return assert_output_close(y_gpu, y_ref, what)
+        return assert_output_close(y_gpu, y_ref, what, round_allow)
     except AssertionError:
         pass
     rms = math.sqrt(float(np.mean(y_ref * y_ref)))
@@ -303,7 +313,8 @@ def assert_output_close_flips(y_gpu: np.ndarray, ref: dict, W, mode: str, K: int
     pos = {int(r): i for i, r in enumerate(ref["a_routes"])}
     g_t = ref.get("a2q", {}).get("g", [0.0])[0]
     toks = ref["tokens"]
-    bad = np.where(np.abs(y_gpu - y_exp).max(1) > MAX_ERR_RMS * rms)[0]
+    excess = np.abs(y_gpu - y_exp) - (BF16_U * np.abs(y_exp) if round_allow else 0.0)
+    bad = np.where(excess.max(1) > MAX_ERR_RMS * rms)[0]
     taken = considered = 0
     for row in bad:
         t = int(toks[row])
@@ -331,4 +342,5 @@ def assert_output_close_flips(y_gpu: np.ndarray, ref: dict, W, mode: str, K: int
                     y_exp[row] += eff
                     taken += 1
     return assert_output_close(
-        y_gpu, y_exp, f"{what} ({taken} of {considered} ambiguous FC2-input roundings re-taken)")
+        y_gpu, y_exp, f"{what} ({taken} of {considered} ambiguous FC2-input roundings re-taken)",
+        round_allow)

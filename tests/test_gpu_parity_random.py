@@ -6,7 +6,11 @@ sample reaches the launch configurations the fixed cases may miss: every
 M-tile size (chosen from the mean rows per expert), weight column counts that
 are and are not multiples of 256 and 512, ragged expert groups and empty
 experts. Every case checks routing and permutation bit-exactly, the FC1-input
-and FC2-input quantization, and the output against the oracle's bar.
+and FC2-input quantization, and the output against the oracle's bar applied
+to the error beyond the output's own bf16 rounding: on some of these shapes
+the heavy-tailed outputs make even the exactly rounded oracle miss the plain
+max-error bar (its largest |y| reaches 9 rms), which the five workloads'
+tests keep.
 """
 import numpy as np
 import pytest
@@ -25,6 +29,7 @@ MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
 
 
 def _cases(n=24, seed=20261202):
+    """Small shapes: every M-tile size, ragged groups, empty experts."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -37,18 +42,39 @@ def _cases(n=24, seed=20261202):
         mode = MODES[i % len(MODES)]
         on_input = bool(rng.integers(0, 2))
         det = bool(rng.integers(0, 4) != 0)  # mostly deterministic, some fused
-        out.append((i, T, H, I, E, K, act, mode, on_input, det))
+        logits = str(rng.choice(["normal", "uniform", "zipf"]))
+        out.append((i, T, H, I, E, K, act, mode, on_input, det, logits))
     return out
 
 
-@pytest.mark.parametrize("case", _cases(), ids=lambda c: f"case{c[0]}")
+def _big_cases(n=8, seed=7):
+    """Wider shapes: 128-row tiles with 512-column blocks (eight waves), skewed
+    groups of several tiles."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([16, 32, 64]))
+        K = int(rng.choice([4, 8]))
+        T = int(rng.choice([512, 1024]))
+        H = int(rng.choice([512, 768, 1024]))
+        I = int(rng.choice([256, 512]))
+        act = str(rng.choice(["swiglu", "relu2"]))
+        mode = MODES[i % len(MODES)]
+        on_input = bool(rng.integers(0, 2))
+        det = bool(rng.integers(0, 4) != 0)
+        logits = str(rng.choice(["normal", "zipf"]))
+        out.append((100 + i, T, H, I, E, K, act, mode, on_input, det, logits))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases() + _big_cases(), ids=lambda c: f"case{c[0]}")
 def test_random_shape(case):
-    i, T, H, I, E, K, act, mode, on_input, det = case
-    what = f"case{i} T={T} H={H} I={I} E={E} K={K} {act} {mode} on_input={on_input} det={det}"
+    i, T, H, I, E, K, act, mode, on_input, det, logits = case
+    what = f"case{i} T={T} H={H} I={I} E={E} K={K} {act} {mode} on_input={on_input} det={det} {logits}"
     print(what, flush=True)
-    inp = Inputs(T, H, I, E, K, act, "normal", seed=100 + i)
+    inp = Inputs(T, H, I, E, K, act, logits, seed=100 + i)
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, T, K, mode, ref)
     check_x_quant(d, ws, T, K, mode, ref)
     check_fc2_input(moe, d, ws, T, K, mode, ref, what)
-    assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what)
+    assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what, round_allow=True)
