@@ -67,7 +67,27 @@ def _big_cases(n=8, seed=7):
     return out
 
 
-@pytest.mark.parametrize("case", _cases() + _big_cases(), ids=lambda c: f"case{c[0]}")
+def _route_cases(n=8, seed=11):
+    """Many experts and routes: the multi-block permutation (more than 16384
+    routes or more than 256 experts) and every routing width (E up to 1024)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([128, 200, 256, 300, 512, 1024]))
+        K = int(rng.choice([1, 2, 6, 9, 16]))
+        T = int(rng.choice([64, 700, 2048, 2500]))
+        H = int(rng.choice([128, 256]))
+        I = int(rng.choice([128, 256]))
+        act = str(rng.choice(["swiglu", "relu2"]))
+        mode = MODES[i % len(MODES)]
+        on_input = bool(rng.integers(0, 2))
+        det = bool(rng.integers(0, 4) != 0)
+        logits = str(rng.choice(["normal", "uniform", "zipf"]))
+        out.append((200 + i, T, H, I, E, K, act, mode, on_input, det, logits))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases() + _big_cases() + _route_cases(), ids=lambda c: f"case{c[0]}")
 def test_random_shape(case):
     i, T, H, I, E, K, act, mode, on_input, det, logits = case
     what = f"case{i} T={T} H={H} I={I} E={E} K={K} {act} {mode} on_input={on_input} det={det} {logits}"
