@@ -98,3 +98,24 @@ def test_random_shape(case):
     check_x_quant(d, ws, T, K, mode, ref)
     check_fc2_input(moe, d, ws, T, K, mode, ref, what)
     assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what, round_allow=True)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_workspace_reuse_across_shapes(mode):
+    """A workspace sized for a large batch, reused for a smaller one right after:
+    the second forward matches a forward on a fresh workspace bit for bit
+    (deterministic finalize) and the oracle, so no state leaks between calls."""
+    E, K, H, I = 24, 4, 256, 128
+    big = Inputs(300, H, I, E, K, "swiglu", "zipf", seed=7)
+    small = Inputs(37, H, I, E, K, "swiglu", "normal", seed=8)
+    d = moe.Dims(E, H, I, "swiglu", "mxfp8" if mode == "mxfp8" else "nvfp4")
+    blob = moe.prepare_weights(d, small.w1, small.w2)
+    ws = torch.empty(moe.workspace_bytes(d, 300, K, mode), dtype=torch.uint8, device="cuda")
+    moe.forward(d, blob, big.x, big.logits, K, mode, True, True, workspace=ws)
+    y_reused = moe.forward(d, blob, small.x, small.logits, K, mode, True, True, workspace=ws).clone()
+    y_fresh = moe.forward(d, blob, small.x, small.logits, K, mode, True, True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_reused.view(torch.int16), y_fresh.view(torch.int16)), f"{mode}: reused workspace differs"
+    _, _, _, y, ref, W = run_layer(small, K, mode, True, True)
+    assert torch.equal(y.view(torch.int16), y_fresh.view(torch.int16))
+    assert_output_close_flips(bf16_to_f64(y_reused), ref, W, mode, K, True, f"reuse {mode}")
