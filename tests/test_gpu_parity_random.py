@@ -119,3 +119,30 @@ def test_workspace_reuse_across_shapes(mode):
     _, _, _, y, ref, W = run_layer(small, K, mode, True, True)
     assert torch.equal(y.view(torch.int16), y_fresh.view(torch.int16))
     assert_output_close_flips(bf16_to_f64(y_reused), ref, W, mode, K, True, f"reuse {mode}")
+
+
+def test_concurrent_forwards_share_a_blob():
+    """Two streams run forwards on one prepared blob with their own workspaces
+    at the same time; each result equals the same forward run alone."""
+    E, K, H, I, mode = 16, 2, 256, 128, "w4a4_tensor"
+    a = Inputs(200, H, I, E, K, "swiglu", "normal", seed=21)
+    b = Inputs(90, H, I, E, K, "swiglu", "zipf", seed=22)
+    d = moe.Dims(E, H, I, "swiglu", "nvfp4")
+    blob = moe.prepare_weights(d, a.w1, a.w2)
+    ya0 = moe.forward(d, blob, a.x, a.logits, K, mode, False, True).clone()
+    yb0 = moe.forward(d, blob, b.x, b.logits, K, mode, False, True).clone()
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    wa = torch.empty(moe.workspace_bytes(d, 200, K, mode), dtype=torch.uint8, device="cuda")
+    wb = torch.empty(moe.workspace_bytes(d, 90, K, mode), dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            ya = moe.forward(d, blob, a.x, a.logits, K, mode, False, True, workspace=wa, stream=s1)
+        with torch.cuda.stream(s2):
+            yb = moe.forward(d, blob, b.x, b.logits, K, mode, False, True, workspace=wb, stream=s2)
+        torch.cuda.synchronize()
+        outs.append((ya.clone(), yb.clone()))
+    for ya, yb in outs:
+        assert torch.equal(ya.view(torch.int16), ya0.view(torch.int16))
+        assert torch.equal(yb.view(torch.int16), yb0.view(torch.int16))
