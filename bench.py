@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_w4a16_T256_H2048_I1024_E64_K6")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=24)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
     ap.add_argument("--copies", type=int, default=0, help="prepared weight copies (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC calibration)")
@@ -100,6 +100,26 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
 
 
+def routing_summary(counts):
+    """The realized expert histogram in brief (rows per expert)."""
+    import numpy as np
+    c = np.sort(np.asarray(counts, dtype=np.int64))[::-1]
+    return {"max_rows": int(c[0]), "mean_rows": round(float(c.mean()), 2),
+            "empty_experts": int((c == 0).sum()), "top3_rows": [int(v) for v in c[:3]],
+            "groups_under_16_rows": int(((c > 0) & (c < 16)).sum())}
+
+
+def host_cpu():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, x, logits, w1, w2, sample_tokens):
     """The oracle (as it stands) on a sample of the same workload: weights are
     quantized first (not timed, like the GPU's preparation); then S1..S7 of the
@@ -123,6 +143,7 @@ def cpu_baseline(wl, x, logits, w1, w2, sample_tokens):
     R.forward(xb, lg, W, wl.K, wl.mode, wl.act, wl.on_input, tokens=toks, threads=1)
     dt = time.perf_counter() - t0
     return {"value": len(toks) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "host_cpu": host_cpu(),
             "sample": f"{len(toks)} of {T} tokens (all {wl.K} routes each), single thread; "
                       f"weights quantized beforehand, not timed; {dt:.1f} s"}
 
@@ -281,7 +302,8 @@ def main():
                    "router_weight_on_input": wl.on_input,
                    "finalize": "deterministic" if True in results else "fused",
                    "timing": "hipGraph replay of one forward per step",
-                   "weight_copies_rotated": copies, "touched_experts": touched},
+                   "weight_copies_rotated": copies, "touched_experts": touched,
+                   "routing": routing_summary(counts)},
         "eager_ms_per_step": round(ms_eager, 5),
         "graph_step_ms_percentiles": pct_det,
         "stages_us": {k: round(v * 1e3, 2) for k, v in st_det.items()},
