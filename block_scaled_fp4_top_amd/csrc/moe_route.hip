@@ -282,13 +282,13 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 }
 
 
-// Small batches (R <= 16384 routes, E <= 256): histogram, scans and the
+// Small batches (R <= 4096 routes, E <= 256): histogram, scans and the
 // stable scatter in one block of 1024 threads (16 waves), saving two
 // launches. Same results as the multi-block path: the scatter walks the
 // routes in order, 1024 at a time, with in-wave ballot ranks and per-wave
 // counts in LDS.
 constexpr int kSmallMaxE = 256;
-constexpr int kSmallMaxR = 16384;
+constexpr int kSmallMaxR = 4096;
 
 __global__ __launch_bounds__(1024) void permute_small_kernel(
     const int32_t* __restrict__ ids, int R, int E, int32_t* __restrict__ counts,

@@ -1,4 +1,4 @@
-"""The five synthetic MoE-layer workloads (shapes, modes and input recipes).
+"""The synthetic MoE-layer workloads (shapes, modes and input recipes).
 
 They stand in for the serving workloads the pages measure (vLLM cells on
 DeepSeek-V4 checkpoints), which need trained weights and datasets that are not
@@ -50,6 +50,10 @@ WORKLOADS = {
                  "w4a4_tensor", "relu2", True, ("det",), "uniform"),
         Workload("prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8", 16384, 7168, 2048, 256, 8,
                  "mxfp8", "swiglu", False, ("fused",), "zipf"),
+        # one GPU's share of the MXFP8 prefill under 8-way expert parallelism:
+        # 32 local experts and an eighth of the routes (same mean group size)
+        Workload("ep8_share_mxfp8_zipf_T2048_H7168_I2048_E32_K8", 2048, 7168, 2048, 32, 8,
+                 "mxfp8", "swiglu", False, ("det", "fused"), "zipf"),
     ]
 }
 
