@@ -19,7 +19,7 @@ TOPW_REL = 1e-6
 # The output is bf16 by the interface: rounding even the exact result costs up
 # to BF16_U * |y| per element (unit roundoff 2^-8). On heavy-tailed outputs
 # that alone can exceed 2e-2 * rms (measured up to 2.5e-2 on shapes outside
-# the five workloads), so tests of arbitrary shapes bound the error beyond it.
+# the named workloads), so tests of arbitrary shapes bound the error beyond it.
 BF16_U = 2.0 ** -8
 
 

@@ -9,7 +9,7 @@ experts. Every case checks routing and permutation bit-exactly, the FC1-input
 and FC2-input quantization, and the output against the oracle's bar applied
 to the error beyond the output's own bf16 rounding: on some of these shapes
 the heavy-tailed outputs make even the exactly rounded oracle miss the plain
-max-error bar (its largest |y| reaches 9 rms), which the five workloads'
+max-error bar (its largest |y| reaches 9 rms), which the named workloads'
 tests keep.
 """
 import numpy as np
