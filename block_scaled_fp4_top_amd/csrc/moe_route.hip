@@ -313,7 +313,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
     __syncthreads();
     const int run = tid < E ? cnt[tid] : 0;
     // expert offsets and the four tile-list offsets in one pass: all prefix
-    // sums stay below 2^16 here (R <= 16384, tiles <= R/16 + E), so two
+    // sums stay below 2^16 here (R <= kSmallMaxR, tiles <= R/16 + E), so two
     // scans share each 32-bit word
     int nt[kNumBM];
 #pragma unroll
