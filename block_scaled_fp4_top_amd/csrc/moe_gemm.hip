@@ -239,16 +239,34 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
-    // Block order: M-tile fastest (across experts), then N-block; consecutive
-    // positions go to the same XCD (blocks are dealt round-robin over the 8
-    // XCDs and the grid is a multiple of 8). Each XCD then sweeps all M-tiles
-    // for its own N-blocks: the blocks it runs at a time share one N-block's
-    // weight columns in its L2, and the eight XCDs walk the A rows in step, so
-    // the shared last-level cache serves most A re-reads.
-    const int total = gridDim.x;
-    const int id = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
-    const int mt = id % p.mt_max, nb = id / p.mt_max;
-    if (nb >= p.N / (16 * NW * WN) || mt >= p.tiles[p.E]) return;
+    // Block order. Blocks are dealt round-robin over the 8 XCDs (each with its
+    // own L2) and the grid is a multiple of 8, so blockIdx % 8 names the XCD.
+    //  - Wide tiles: M-tile fastest (across experts), then N-block, in
+    //    consecutive positions per XCD. Each XCD sweeps all M-tiles for its own
+    //    N-blocks: the blocks it runs at a time share one N-block's weight
+    //    columns in its L2 (re-read by the M-tiles of an expert), and the eight
+    //    XCDs walk the A rows in step, so the last-level cache serves most A
+    //    re-reads.
+    //  - Small tiles (every weight is read once): the active (M-tile, N-block)
+    //    pairs, N-block fastest, are cut into 8 contiguous ranges, one per XCD.
+    //    All N-blocks of an M-tile then run on one XCD, so its A rows come into
+    //    one L2 once instead of into all eight.
+    int mt, nb;
+    if constexpr (BM <= 32) {
+        const int NB = p.N / (16 * NW * WN);
+        const int work = p.tiles[p.E] * NB;  // <= the grid: tiles[E] <= mt_max
+        const int per = (work + 7) >> 3;
+        const int j = blockIdx.x >> 3;
+        const int w = (blockIdx.x & 7) * per + j;
+        if (j >= per || w >= work) return;
+        mt = w / NB;
+        nb = w % NB;
+    } else {
+        const int id = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        mt = id % p.mt_max;
+        nb = id / p.mt_max;
+        if (nb >= p.N / (16 * NW * WN) || mt >= p.tiles[p.E]) return;
+    }
     int lo = 0, hi = p.E - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
