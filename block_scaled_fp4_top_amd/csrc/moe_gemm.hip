@@ -14,6 +14,9 @@
 //    so each load is a contiguous 1 KB (NVFP4) or 2 KB (MXFP8) per wave.
 //  - P-stage software pipeline: the loads of the next P-1 steps are in flight
 //    while one step is multiplied (P LDS buffers for A, P register sets for B).
+//  - Small tiles (decode): one contiguous range of tiles per XCD, and, when
+//    every block is resident at once, wave priorities that let the blocks
+//    furthest behind in their K loop issue first.
 //  - NVFP4: exact dequantization code * sf in registers (hardware fp4
 //    converter at unit scale, then the E4M3 block scale: a packed fp16 multiply
 //    for fp16 operands, an fp32 multiply for bf16; the product has at most 6
@@ -30,6 +33,7 @@
 //    token accumulator (fused finalize).
 #include <hip/hip_ext.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -252,6 +256,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     //    All N-blocks of an M-tile then run on one XCD, so its A rows come into
     //    one L2 once instead of into all eight.
     int mt, nb;
+    bool fair = false;  // see the wave priorities in the K loop
     if constexpr (BM <= 32) {
         const int NB = p.N / (16 * NW * WN);
         const int work = p.tiles[p.E] * NB;  // <= the grid: tiles[E] <= mt_max
@@ -261,6 +266,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         if (j >= per || w >= work) return;
         mt = w / NB;
         nb = w % NB;
+        fair = work <= p.resident;
     } else {
         const int id = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
         mt = id % p.mt_max;
@@ -478,9 +484,24 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         // flight, then refills the buffer freed by step kt - 1. Full groups of P
         // steps run without branches between them, so every buffer keeps its
         // registers across the loop; the remaining steps follow after it.
+        // Wave priorities (small tiles whose blocks are all resident at once):
+        // the instruction arbiter favours older waves, so the blocks a CU
+        // received first would stream ahead and the last ones would finish
+        // late, with the chip's loads thinning out meanwhile. Each block's
+        // waves instead run at priority 3, 2, 1, 0 over the four quarters of
+        // their K loop, so blocks that are behind issue first.
+        auto set_prio = [&](int kt) {
+            const int q = (4 * kt) / KT;
+            if (kt != 0 && q == (4 * (kt - 1)) / KT) return;
+            if (q == 0) __builtin_amdgcn_s_setprio(3);
+            else if (q == 1) __builtin_amdgcn_s_setprio(2);
+            else if (q == 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        };
         auto step = [&](int kt, int u) {
             wait_vmcnt<L * (P - 2)>();
             bare_barrier();
+            if (BM <= 32 && fair) set_prio(kt);
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
                 reg_fence(rc[u][s]);
@@ -522,11 +543,32 @@ static void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, hipEven
     else hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
 }
 
+// Blocks of `kernel` the current device holds at once (occupancy x CUs), cached
+// per device; 0 if the runtime cannot say.
+template <typename K>
+static int resident_blocks(K kernel, int threads) {
+    static std::atomic<int> cache[64];  // value + 1; 0 = not yet asked
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        c = per_cu * cus + 1;
+        cache[dev].store(c, std::memory_order_relaxed);
+    }
+    return c - 1;
+}
+
 template <int AB, int EPI, int BM, int WN, int P, int NW>
 static void launch_cfg(const GemmArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
     const long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
     const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(NW * 64);
-    launch_timed(gemm_kernel<AB, BM, WN, EPI, P, NW>, grid, block, s, t0, t1, a);
+    GemmArgs b = a;
+    b.resident = resident_blocks(gemm_kernel<AB, BM, WN, EPI, P, NW>, NW * 64);
+    launch_timed(gemm_kernel<AB, BM, WN, EPI, P, NW>, grid, block, s, t0, t1, b);
 }
 
 template <int AB, int EPI>

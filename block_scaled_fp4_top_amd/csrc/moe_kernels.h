@@ -66,6 +66,7 @@ struct GemmArgs {
     const int32_t* tiles;  // [E+1] for this BM
     int E;
     int mt_max;
+    int resident;  // set by the launcher: blocks of this kernel the device holds at once
     // epilogue
     int act, on_input, I;
     const float* topw;
