@@ -406,6 +406,9 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     g2.out_f32 = WS(float, V_O);
     g2.yacc = WS(float, V_YACC);
     g2.fused = fused;
+    // a token accumulator well above the 256 MB last-level cache: N-block-major
+    // FC2 order, so each phase's atomics stay in cache
+    g2.phased = fused && (size_t)T * H * 4 > kPhasedYaccBytes;
     timer_kernel_events(5, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream, t0, t1), "FC2");
 

@@ -251,6 +251,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     //    columns in its L2 (re-read by the M-tiles of an expert), and the eight
     //    XCDs walk the A rows in step, so the last-level cache serves most A
     //    re-reads.
+    //  - Wide tiles, FC2 with the fused finalize into a token accumulator larger
+    //    than the last-level cache: N-block slowest for the whole chip (every
+    //    XCD takes one contiguous range of M-tiles per N-block), so the
+    //    atomics of a phase land on one N-block's columns of the accumulator
+    //    (T x 512 x 4 bytes), which stay cache-resident; an expert's M-tiles
+    //    still share one XCD's L2 for their weights.
     //  - Small tiles (every weight is read once): the active (M-tile, N-block)
     //    pairs, N-block fastest, are cut into 8 contiguous ranges, one per XCD.
     //    All N-blocks of an M-tile then run on one XCD, so its A rows come into
@@ -267,6 +273,14 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         mt = w / NB;
         nb = w % NB;
         fair = work <= p.resident;
+    } else if (EPI == EPI_FC2 && p.phased) {
+        const int NB = p.N / (16 * NW * WN);
+        const int act = p.tiles[p.E];
+        const int per = (act + 7) >> 3;
+        const int j = blockIdx.x >> 3;
+        nb = j / per;
+        mt = (blockIdx.x & 7) * per + j % per;
+        if (nb >= NB || mt >= act) return;
     } else {
         const int id = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
         mt = id % p.mt_max;
@@ -564,7 +578,9 @@ static int resident_blocks(K kernel, int threads) {
 
 template <int AB, int EPI, int BM, int WN, int P, int NW>
 static void launch_cfg(const GemmArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    const long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
+    long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
+    if (BM > 32 && EPI == EPI_FC2 && a.phased)  // room for 8 ranges of ceil(mt_max / 8) per N-block
+        blocks = 8LL * (a.N / (16 * NW * WN)) * ((a.mt_max + 7) / 8);
     const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(NW * 64);
     GemmArgs b = a;
     b.resident = resident_blocks(gemm_kernel<AB, BM, WN, EPI, P, NW>, NW * 64);

@@ -109,6 +109,10 @@ constexpr int kAmaxSlots = 32, kAmaxStride = 32;
 constexpr int kMiscXAmax = 0, kMiscA2Amax = kAmaxSlots * kAmaxStride;
 constexpr int kMiscWords = 2 * kAmaxSlots * kAmaxStride;
 
+// The fused FC2 switches to its N-block-major block order when the fp32 token
+// accumulator T x H exceeds this (half the 256 MB last-level cache).
+constexpr size_t kPhasedYaccBytes = 128ull << 20;
+
 enum WsView {
     V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,

@@ -77,6 +77,7 @@ struct GemmArgs {
     uint32_t* amax_slot; // FC1: kAmaxSlots partial maxima of the FC2 input, kAmaxStride apart (NVFP4 per-tensor)
     float* yacc;         // FC2 fused: [T][N]
     int fused;
+    int phased;          // FC2 fused on wide tiles: N-block-major block order (large y_acc)
 };
 
 // t0/t1: optional events recorded at the kernel's start and end.
