@@ -277,6 +277,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         const int NB = p.N / (16 * NW * WN);
         const int act = p.tiles[p.E];
         const int per = (act + 7) >> 3;
+        if (per == 0) return;  // no rows (a forward always has some)
         const int j = blockIdx.x >> 3;
         nb = j / per;
         mt = (blockIdx.x & 7) * per + j % per;
