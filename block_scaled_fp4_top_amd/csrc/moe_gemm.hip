@@ -288,12 +288,28 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         nb = id / p.mt_max;
         if (nb >= p.N / (16 * NW * WN) || mt >= p.tiles[p.E]) return;
     }
-    int lo = 0, hi = p.E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+    // Expert of M-tile mt: the last e with tiles[e] <= mt (tiles[] is the
+    // exclusive prefix of the experts' tile counts, so empty experts repeat
+    // their successor's entry and are skipped).
+    int e;
+    if constexpr (BM <= 32) {
+        // one wave-wide load and ballot per 64 experts instead of a chain of
+        // dependent loads: these blocks are all resident at once, so their
+        // start-up latency is on the kernel's critical path
+        int cnt = 0;
+        for (int base = 0; base < p.E; base += 64) {
+            const int ee = base + lane;
+            cnt += __popcll(__ballot(ee < p.E && p.tiles[ee] <= mt));
+        }
+        e = cnt - 1;
+    } else {
+        int lo = 0, hi = p.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
     }
-    const int e = lo;
     const int mt_local = mt - p.tiles[e];
     const int row0 = p.offsets[e] + mt_local * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
@@ -617,9 +633,15 @@ static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s, hipE
             else launch_cfg<AB, EPI, 64, 2, 2, 4>(a, s, t0, t1);
             break;
         default:
-            if (a.N % 256 != 0) launch_cfg<AB, EPI, 128, 2, 2, 4>(a, s, t0, t1);
-            else if (AB != AB_BF16_NV && a.N % 512 == 0) launch_cfg<AB, EPI, 128, 4, PW8, 8>(a, s, t0, t1);
-            else launch_cfg<AB, EPI, 128, 4, PW, 4>(a, s, t0, t1);
+            if (a.N % 256 != 0) {
+                launch_cfg<AB, EPI, 128, 2, 2, 4>(a, s, t0, t1);
+            } else if (a.N % 512 == 0) {
+                // (not instantiated for bf16 operands: that variant spills)
+                if constexpr (AB != AB_BF16_NV) launch_cfg<AB, EPI, 128, 4, PW8, 8>(a, s, t0, t1);
+                else launch_cfg<AB, EPI, 128, 4, PW, 4>(a, s, t0, t1);
+            } else {
+                launch_cfg<AB, EPI, 128, 4, PW, 4>(a, s, t0, t1);
+            }
             break;
     }
     return hipGetLastError();
