@@ -259,22 +259,32 @@ def test_fused_matches_deterministic():
         assert_output_close(yf, yd, f"fused vs det {mode}")
 
 
-def test_standalone_finalize():
-    T, K, H = 37, 5, 384
-    g = torch.Generator().manual_seed(7)
+@pytest.mark.parametrize("T,K,H", [(37, 5, 384), (9, 3, 2052), (2100, 2, 260)])
+def test_standalone_finalize(T, K, H):
+    """moe_finalize against the oracle's sequential finalize, fp32 and bf16 O:
+    one block per token (T >= 2048) and per token and 1024-column chunk with
+    a partial last chunk (H = 2052)."""
+    g = torch.Generator().manual_seed(7 + T)
     O = torch.randn(T * K, H, generator=g)
     perm = torch.randperm(T * K, generator=g).to(torch.int32)
     w = torch.rand(T, K, generator=g)
-    for weights in (w, None):
-        y = moe.finalize(O.cuda(), perm.cuda(), None if weights is None else weights.cuda(), T, K)
-        torch.cuda.synchronize()
+
+    def ref_of(O64, weights):
         ref = np.empty((T, H))
-        R.lib().orc_finalize(T, K, H, R._p(O.double().numpy()), R._p(perm.numpy()),
+        R.lib().orc_finalize(T, K, H, R._p(O64), R._p(perm.numpy()),
                              None if weights is None else R._p(weights.double().numpy()),
                              R._p(ref))
-        yg = bf16_to_f64(y)
-        # one bf16 rounding of an fp32 sum of K terms
-        bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(O.numpy()).max() * K
-        assert np.all(np.abs(yg - ref) <= bound)
-        yb = moe.finalize(O.cuda().bfloat16(), perm.cuda(), None, T, K)
-        assert yb.shape == (T, H)
+        return ref
+
+    for weights in (w, None):
+        for o_bf16 in (False, True):
+            Od = O.cuda().bfloat16() if o_bf16 else O.cuda()
+            y = moe.finalize(Od, perm.cuda(), None if weights is None else weights.cuda(), T, K)
+            torch.cuda.synchronize()
+            O64 = (O.bfloat16() if o_bf16 else O).double().numpy()
+            ref = ref_of(np.ascontiguousarray(O64), weights)
+            yg = bf16_to_f64(y)
+            assert yg.shape == (T, H)
+            # one bf16 rounding of an fp32 sum of K terms
+            bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * np.abs(O64).max() * K
+            assert np.all(np.abs(yg - ref) <= bound), (T, K, H, weights is None, o_bf16)
