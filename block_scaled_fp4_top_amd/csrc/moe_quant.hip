@@ -56,7 +56,9 @@ __device__ __forceinline__ void nvfp4_deq_f16(const uint32_t* packed, uint32_t s
 }
 
 // WPR waves per row: 1 (four rows per block) or 4 (one row per block, for
-// few wide rows).
+// few wide rows). With a tensor-wide or no global scale the blocks of a row
+// are independent, and gridDim.y > 1 splits each row into chunks of
+// 64 * WPR quantization blocks (few rows: more blocks in flight).
 template <int KIND, bool BF16, int WPR>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ v, int rows,
                                                          int cols,
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     const size_t base = (size_t)row * cols;
     if (KIND == QK_MX) {
         const int nb = cols / 32;
-        for (int b = lt; b < nb; b += TPR) {
+        const int b_end = gridDim.y == 1 ? nb : min(nb, ((int)blockIdx.y + 1) * TPR);
+        for (int b = blockIdx.y * TPR + lt; b < b_end; b += TPR) {
             float vv[32];
             load16<BF16>(v, base + (size_t)b * 32, vv);
             load16<BF16>(v, base + (size_t)b * 32 + 16, vv + 16);
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
         const int ln = tid & 63;
         const float am = wave_max(ln < amax_slots ? u2f(amax_slot[(size_t)ln * amax_stride]) : 0.0f);
         gg = __fdiv_rn(am, 2688.0f);
-        if (row == 0 && lt == 0) g[0] = gg;
+        if (row == 0 && lt == 0 && blockIdx.y == 0) g[0] = gg;
     } else {
         float m = 0.0f;
         for (int i = lt; i < cols; i += TPR) m = fmaxf(m, fabsf(load1<BF16>(v, base + i)));
@@ -108,7 +111,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
         if (lt == 0) g[row] = gg;
     }
     const int nb = cols / 16;
-    for (int b = lt; b < nb; b += TPR) {
+    const int b_end = gridDim.y == 1 ? nb : min(nb, ((int)blockIdx.y + 1) * TPR);
+    for (int b = blockIdx.y * TPR + lt; b < b_end; b += TPR) {
         float vv[16];
         load16<BF16>(v, base + (size_t)b * 16, vv);
         uint32_t packed[2], sf;
@@ -421,7 +425,11 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
         return hipGetLastError();
     }
     const bool wide = rows < 2048 && cols >= 1024;  // few long rows: a block per row
-    const dim3 grid(wide ? rows : (rows + 3) / 4), block(256);
+    // very few rows: also split each row (not for per-row scales, whose row
+    // maximum needs the whole row in one block)
+    const int qb = kind == QK_MX ? 32 : 16;
+    const unsigned chunks = (wide && rows < 256 && kind != QK_NV_ROW) ? (unsigned)((cols / qb + 255) / 256) : 1u;
+    const dim3 grid(wide ? rows : (rows + 3) / 4, chunks), block(256);
 #define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, amax_slots, amax_stride, codes, scales, g, deq)
 #define QRW(KD, BF) do { if (wide) QR(KD, BF, 4); else QR(KD, BF, 1); } while (0)
     if (in_bf16) {

@@ -138,10 +138,12 @@ def _crafted_matrix(rows, cols, seed):
 @pytest.mark.parametrize("kind", ["nvfp4_tensor", "nvfp4_row", "mxfp8"])
 def test_quantizer_bit_exact(kind):
     # shapes reach every row-quantizer variant: few long rows (a block per
-    # row), short rows, and many long rows held in registers (1 and 7 blocks
-    # of 16 per lane, the latter with idle lanes)
+    # row, and rows split into chunks of 256 quantization blocks: 2 chunks for
+    # NVFP4 at 7168 columns, 4 / 2 for NVFP4 / MXFP8 at 16384, partial last
+    # chunks), short rows, and many long rows held in registers (1 and 7
+    # blocks of 16 per lane, the latter with idle lanes)
     for rows, cols, seed in [(7, 256, 1), (33, 2048, 2), (3, 7168, 3), (2080, 1024, 4),
-                             (2049, 7168, 5)]:
+                             (2049, 7168, 5), (5, 16384, 6), (3, 12320, 7)]:
         v = _crafted_matrix(rows, cols, seed)
         codes, scales, g = moe.quantize(v.cuda(), kind)
         torch.cuda.synchronize()
