@@ -124,40 +124,59 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
     for (int e = threadIdx.x; e < E; e += 256) bhist[(size_t)blockIdx.x * E + e] = h[e];
 }
 
-// Exclusive scan over the threads of a 1024-thread block: an inclusive scan
-// inside each wave by lane shuffles, then the preceding waves' totals from
-// LDS (two barriers in all).
-__device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*>= 16 ints*/) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) buf[w] = x;
-    __syncthreads();
-    int before = 0;
-    for (int i = 0; i < w; ++i) before += buf[i];
-    __syncthreads();  // buf may be reused by the next scan
-    return before + x - v;
+// Inclusive scan over the 64 lanes of a wave with DPP moves: row_shr 1, 2, 4,
+// 8 inside each 16-lane row (lanes shifted in from outside the row read 0),
+// then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3, and
+// row_bcast:31 adds the total of rows 0-1 to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+    return v;
 }
 
-// Three independent exclusive scans at once (same scheme, two barriers).
-__device__ __forceinline__ int3 block1024_exclusive_scan3(int3 v, int* buf /*>= 48 ints*/) {
+// Exclusive scan over the threads of a 1024-thread block: a DPP scan inside
+// each wave, the 16 wave totals scanned by wave 0, two barriers. The totals
+// (buf[0, 16)) and the wave prefixes (buf[16, 32)) are separate, so a second
+// scan may reuse buf right away.
+__device__ __forceinline__ int block1024_exclusive_scan(int v, int* buf /*>= 32 ints*/) {
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    int3 x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int a = __shfl_up(x.x, off), b = __shfl_up(x.y, off), c = __shfl_up(x.z, off);
-        if (lane >= off) { x.x += a; x.y += b; x.z += c; }
+    const int x = wave_incl_scan(v);
+    if (lane == 63) buf[w] = x;
+    __syncthreads();
+    if (w == 0) {
+        const int a = lane < 16 ? buf[lane] : 0;
+        const int ia = wave_incl_scan(a);
+        if (lane < 16) buf[16 + lane] = ia - a;
     }
+    __syncthreads();
+    return buf[16 + w] + x - v;
+}
+
+// Three independent exclusive scans at once (same scheme, two barriers;
+// totals in buf[0, 48), wave prefixes in buf[48, 96)).
+__device__ __forceinline__ int3 block1024_exclusive_scan3(int3 v, int* buf /*>= 96 ints*/) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int3 x = make_int3(wave_incl_scan(v.x), wave_incl_scan(v.y), wave_incl_scan(v.z));
     if (lane == 63) { buf[3 * w] = x.x; buf[3 * w + 1] = x.y; buf[3 * w + 2] = x.z; }
     __syncthreads();
-    int3 before = make_int3(0, 0, 0);
-    for (int i = 0; i < w; ++i) { before.x += buf[3 * i]; before.y += buf[3 * i + 1]; before.z += buf[3 * i + 2]; }
+    if (w == 0) {
+        const int a = lane < 16 ? buf[3 * lane] : 0;
+        const int b = lane < 16 ? buf[3 * lane + 1] : 0;
+        const int c = lane < 16 ? buf[3 * lane + 2] : 0;
+        const int ia = wave_incl_scan(a), ib = wave_incl_scan(b), ic = wave_incl_scan(c);
+        if (lane < 16) {
+            buf[48 + 3 * lane] = ia - a;
+            buf[48 + 3 * lane + 1] = ib - b;
+            buf[48 + 3 * lane + 2] = ic - c;
+        }
+    }
     __syncthreads();
-    return make_int3(before.x + x.x - v.x, before.y + x.y - v.y, before.z + x.z - v.z);
+    return make_int3(buf[48 + 3 * w] + x.x - v.x, buf[48 + 3 * w + 1] + x.y - v.y,
+                     buf[48 + 3 * w + 2] + x.z - v.z);
 }
 
 // One block of 1024 threads: per-block bases by a column scan over the block
