@@ -375,8 +375,14 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
         if (valid && rank == 0) wh[w][x] = __popcll(peers);
         __syncthreads();
         if (valid) {
+            // routes of expert x in the earlier waves: all 15 reads issued
+            // together, the later waves' counts masked out
             int prior = 0;
-            for (int ww = 0; ww < w; ++ww) prior += wh[ww][x];
+#pragma unroll
+            for (int ww = 0; ww < 15; ++ww) {
+                const int c = wh[ww][x];
+                prior += ww < w ? c : 0;
+            }
             const int row = cnt[x] + prior + rank;
             if (row >= 0 && row < R) {
                 r2r[row] = r;
