@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const void* __restrict__ 
     __shared__ int32_t s_row[kMaxK];
     __shared__ float s_w[kMaxK];
     const int t = blockIdx.x;
-    if (threadIdx.x < K) {
+    if ((int)threadIdx.x < K) {
         s_row[threadIdx.x] = rt2row[(size_t)t * K + threadIdx.x];
         s_w[threadIdx.x] = w ? w[(size_t)t * K + threadIdx.x] : 1.0f;
     }
