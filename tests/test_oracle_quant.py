@@ -116,3 +116,32 @@ def test_mxfp8_roundtrip():
     deq = R.mxfp8_dequant(codes, sc)
     c2, s2 = R.mxfp8_quantize(deq.astype(np.float32))
     assert np.array_equal(s2, sc) and np.array_equal(c2, codes)
+
+
+def test_nvfp4_operation_order_non_power_of_two_g():
+    """Pin of the fp32 operation order at a global scale that is not a power of
+    two (g = fl32(1/2688)): the golden row was derived with exact rationals and
+    hand-written IEEE binary32 rounding (tests/golden/make_nvfp4_order_case.py),
+    independently of the oracle. Three plausible slips, s = (a_b/6)/g, d kept
+    exact in fp64, and v * (1/d), each change a scale or code of this row, so
+    the oracle matching the binding order rules them out."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "make_nvfp4_order_case", os.path.join(GOLD, "make_nvfp4_order_case.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    with open(os.path.join(GOLD, "nvfp4_order_nonpow2_g.json")) as f:
+        ex = json.load(f)
+    assert ex["orders"] == mk.derive(), "golden file out of date with its derivation"
+    exp = ex["orders"]["reading8"]
+    for order, alt in ex["orders"].items():
+        if order != "reading8":
+            assert alt["scales"] != exp["scales"] or alt["codes"] != exp["codes"], order
+    row = np.array([float.fromhex(h) for h in ex["row_hex"]], np.float32).reshape(1, -1)
+    g_exp = np.float32(float.fromhex(exp["g_hex"]))
+    assert g_exp != np.float32(2.0 ** np.floor(np.log2(g_exp)))  # not a power of two
+    for per_row in (True, False):
+        codes, sf, g = R.nvfp4_quantize(row, per_row=per_row)
+        assert g[0] == g_exp
+        assert list(sf[0]) == exp["scales"]
+        assert list(codes[0]) == exp["codes"]
