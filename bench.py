@@ -1,13 +1,18 @@
 """Benchmark of one block-scaled MoE layer forward on one MI355X.
 
-Default workload: NVFP4 W4A16 decode layer, T=256 tokens, H=2048, I=1024,
-E=64 experts, top-6, SwiGLU, router weight on the output side, deterministic
-(fixed-order) finalize; the fused-finalize variant is timed beside it.
+Default (the headline line): the MXFP8 W8A8 prefill layer, T=16384 tokens,
+H=7168, I=2048, E=256 experts, top-8, SwiGLU, Zipf(1.1)-skewed routing, router
+weight on the output side, fused finalize (its configured variant); the
+deterministic finalize is timed beside it. The four other workloads (tiny
+NVFP4 W4A4, NVFP4 W4A16 decode, NVFP4 W4A4 per-token prefill, NVFP4 W4A4
+ReLU2 decode) follow as sub-records of the same line.
 
-A step is one moe_forward (routing, permutation, FC1 with fused SwiGLU,
-FC2-input store, FC2, finalize) over resident inputs. Weights are prepared
-once (off the timed path). Several prepared weight copies are rotated so the
-working set exceeds the 256 MB Infinity Cache and weight reads come from HBM.
+A step is one moe_forward (routing, permutation, activation quantization, FC1
+with fused activation, FC2-input quantization, FC2, finalize) over inputs
+already resident in HBM, replayed from a captured hipGraph. Weights are
+prepared once, off the timed path; when a prepared blob is smaller than three
+times the 256 MB Infinity Cache, several copies are rotated so weight reads
+come from HBM.
 
 Prints one JSON line (see --help for options).
 """
@@ -28,32 +33,42 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
 METRIC = "MoE layer tokens/s on 1 MI355X; % MFMA peak (prefill), % HBM BW (decode)"
 MALL_BYTES = 256 << 20
+HEADLINE = "prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8"
+SUBRECORDS = ["tiny_w4a4_tensor_T16_H256_I128_E8_K2", "decode_w4a16_T256_H2048_I1024_E64_K6",
+              "prefill_w4a4_token_T4096_H4096_I2048_E128_K8",
+              "decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8"]
+# oracle sample per workload: tokens of a sub-batch that take about 10-30 s
+# of single-thread CPU time
+CPU_SAMPLE_TOKENS = {"tiny_w4a4_tensor_T16_H256_I128_E8_K2": 16,
+                     "decode_w4a16_T256_H2048_I1024_E64_K6": 48,
+                     "prefill_w4a4_token_T4096_H4096_I2048_E128_K8": 8,
+                     "decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8": 8,
+                     "prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8": 3,
+                     "ep8_share_mxfp8_zipf_T2048_H7168_I2048_E32_K8": 3}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode_w4a16_T256_H2048_I1024_E64_K6")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--no-subrecords", action="store_true",
+                    help="time the headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=48)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = per-workload default")
     ap.add_argument("--copies", type=int, default=0, help="prepared weight copies (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (PMC calibration)")
     return ap.parse_args()
 
 
-def touched_bytes(d, counts, wfmt):
-    """Algorithmic weight bytes of FC1 and FC2 for the experts with rows."""
-    touched = int((counts > 0).sum())
+def weight_bytes(d, wfmt):
+    """Prepared bytes of one expert's W1 and W2 (codes + block scales + global
+    scale)."""
     if wfmt == "nvfp4":
-        b1 = d.N1 * d.H // 2 + d.N1 * d.H // 16 + 4
-        b2 = d.H * d.I // 2 + d.H * d.I // 16 + 4
-    else:
-        b1 = d.N1 * d.H + d.N1 * d.H // 32
-        b2 = d.H * d.I + d.H * d.I // 32
-    return touched, touched * b1, touched * b2
+        return (d.N1 * d.H // 2 + d.N1 * d.H // 16 + 4, d.H * d.I // 2 + d.H * d.I // 16 + 4)
+    return (d.N1 * d.H + d.N1 * d.H // 32, d.H * d.I + d.H * d.I // 32)
 
 
 def kernel_hash():
@@ -70,7 +85,7 @@ def kernel_hash():
 
 def committed_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources."""
+    was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -120,43 +135,70 @@ def host_cpu():
     return None
 
 
-def cpu_baseline(wl, x, logits, w1, w2, sample_tokens):
-    """The oracle (as it stands) on a sample of the same workload: weights are
-    quantized first (not timed, like the GPU's preparation); then S1..S7 of the
-    oracle run single-threaded for the first `sample_tokens` tokens (routing,
-    permutation and x quantization cover all tokens)."""
+def cpu_baseline(wl, x, logits, w1, w2, ntok):
+    """The oracle as it stands, single-threaded, on a sub-batch of the
+    workload: its first `ntok` tokens run as a batch of their own (routing,
+    permutation, quantization, both GEMMs, finalize). The experts those
+    tokens reach are quantized beforehand (not timed, like the GPU's weight
+    preparation)."""
     import numpy as np
     import torch
 
     from oracle import reference as R
-    T = wl.T
-    toks = list(range(min(sample_tokens, T)))
-    xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
-    lg = logits.cpu().numpy()
+    ntok = min(ntok, wl.T)
+    xb = x[:ntok].cpu().view(torch.int16).numpy().view(np.uint16)
+    lg = logits[:ntok].cpu().numpy()
     W = R.QuantWeights(wl.wfmt, wl.E, wl.H, wl.I, wl.act,
                        lambda e: (w1[e].cpu().numpy(), w2[e].cpu().numpy()))
     ids, _ = R.route(lg, wl.K)
-    need = set(int(e) for e in ids.ravel()) if wl.mode == "w4a4_tensor" else \
-        set(int(e) for e in ids[toks].ravel())
-    W.ensure(need, threads=min(16, os.cpu_count() or 1))
+    W.ensure(set(int(e) for e in ids.ravel()), threads=min(16, os.cpu_count() or 1))
     t0 = time.perf_counter()
-    R.forward(xb, lg, W, wl.K, wl.mode, wl.act, wl.on_input, tokens=toks, threads=1)
+    R.forward(xb, lg, W, wl.K, wl.mode, wl.act, wl.on_input, threads=1)
     dt = time.perf_counter() - t0
-    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+    return {"value": round(ntok / dt, 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "host_cpu": host_cpu(),
-            "sample": f"{len(toks)} of {T} tokens (all {wl.K} routes each), single thread; "
-                      f"weights quantized beforehand, not timed; {dt:.1f} s"}
+            "sample": f"the first {ntok} of {wl.T} tokens as a batch of their own (all {wl.K} "
+                      f"routes each, every stage), single thread; experts quantized beforehand, "
+                      f"not timed; {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs all experts on a single MI355X).", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def roofline(wl, d, counts, st_us, decode):
+    """Roofline object for the dominant GEMM of one timed variant.
+
+    Algorithmic bytes per launch (the layer's own data, no intermediates):
+    FC1 = weights of the experts with rows + the layer input x (bf16, T*H*2);
+    FC2 = weights of the experts with rows + the layer output y (bf16, T*H*2).
+    Algorithmic flops per launch: FC1 2*R*N1*H, FC2 2*R*H*I (routed rows only).
+    The duration is the kernel's own average, from HIP events recorded at its
+    start and end on the launch stream in the eager pass."""
+    touched = int((counts > 0).sum())
+    b1, b2 = weight_bytes(d, wl.wfmt)
+    io = wl.T * wl.H * 2
+    R_ = wl.T * wl.K
+    kern = "fc1" if st_us["fc1"] >= st_us["fc2"] else "fc2"
+    kbytes = touched * (b1 if kern == "fc1" else b2) + io
+    kflops = 2.0 * R_ * (wl.N1 * wl.H if kern == "fc1" else wl.H * wl.I)
+    us = st_us[kern]
+    dtype = {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "mxfp8": "fp8"}[wl.mode]
+    if decode:
+        ach = kbytes / (us * 1e-6) / 1e9
+        r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(ach / HBM_PEAK_GBS, 4)}
+    else:
+        ach = kflops / (us * 1e-6) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        r = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+             "frac": round(ach / peak, 4)}
+    r["traffic"] = committed_traffic(wl.name, kern)
+    r["kernel"] = f"gemm_kernel ({kern.upper()})"
+    r["avg_launch_us"] = round(us, 2)
+    r["algorithmic_bytes"] = int(kbytes)
+    r["algorithmic_flops"] = kflops
+    return r
+
+
+def run_workload(name, args, with_cpu):
+    """Times one workload (both finalize variants it runs); returns its record."""
     import numpy as np
     import torch
 
@@ -164,9 +206,8 @@ def main():
     from synth_inputs import WORKLOADS, make_logits, make_x
     from synth_inputs.gen import STREAM_W1, STREAM_W2, make_weight
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[name]
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     d = moe.Dims(wl.E, wl.H, wl.I, wl.act, wl.wfmt)
     x = make_x(wl.seed, wl.T, wl.H, device=dev)
     logits = make_logits(wl.seed, wl.T, wl.E, wl.logits, device=dev)
@@ -181,9 +222,7 @@ def main():
     blobs = [moe.prepare_weights(d, w1, w2) for _ in range(copies)]
     torch.cuda.synchronize()
     moe.check_prepared(d, blobs[0])
-    cpu_w = None
-    if not args.no_cpu_baseline:
-        cpu_w = (w1.cpu(), w2.cpu())
+    cpu_w = (w1.cpu(), w2.cpu()) if with_cpu else None
     del w1, w2
     torch.cuda.empty_cache()
 
@@ -194,24 +233,22 @@ def main():
         moe.forward(d, blobs[i % copies], x, logits, wl.K, wl.mode, wl.on_input, det,
                     workspace=ws, out=y)
 
-    results = {}
-    for det in (True, False):
-        if det is False and "fused" not in wl.finalize:
-            continue
-        # eager pass: per-stage HIP events on the launch stream
+    variants = {}
+    for fin in ("fused", "det"):
+        det = fin == "det"
+        # eager pass: per-stage HIP events on the launch stream (the GEMMs'
+        # events are recorded at their own start and end)
         for i in range(args.warmup):
             step(i, det)
         torch.cuda.synchronize()
         moe.stage_times()  # reset
         moe.stage_timing(True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         for i in range(args.steps):
             step(i, det)
         torch.cuda.synchronize()
-        dt_eager = time.perf_counter() - t0
         moe.stage_timing(False)
         st, nfw = moe.stage_times()
+        assert moe.forward_status(ws) == 0
         # graph pass: one captured forward per weight copy, replayed in turn
         graphs = []
         side = torch.cuda.Stream()
@@ -234,8 +271,8 @@ def main():
         for i in range(args.steps):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
-        dt_graph = time.perf_counter() - t0
-        # distribution: one event pair per replay (outside the timed loop above)
+        dt = time.perf_counter() - t0
+        # per-replay distribution (outside the timed loop above)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         evs[0].record()
         for i in range(args.steps):
@@ -243,85 +280,78 @@ def main():
             evs[i + 1].record()
         torch.cuda.synchronize()
         per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-        pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 5) for q in (10, 50, 90)}
-        results[det] = (dt_graph / args.steps * 1e3, dt_eager / args.steps * 1e3,
-                        {k: v / max(nfw, 1) for k, v in st.items()}, pct)
+        pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 5)
+               for q in (10, 50, 90)}
+        variants[fin] = {"ms": dt / args.steps * 1e3, "pct": pct,
+                         "st_us": {k: v / max(nfw, 1) * 1e3 for k, v in st.items()}}
         del graphs
 
     counts = moe.workspace_view(d, ws, wl.T, wl.K, wl.mode, "counts").cpu().numpy()
-    touched, wb1, wb2 = touched_bytes(d, counts, wl.wfmt)
-    R_ = wl.T * wl.K
-    # algorithmic bytes per launch (see the design notes): weights of the
-    # touched experts, the kernel's activation input once, its output once
-    x_in = wl.T * wl.H * (2 if wl.mode == "w4a16" else (1 if wl.mode == "mxfp8" else 0.5 + 1 / 16))
-    fc1_out = R_ * wl.I * (2 if wl.mode == "w4a16" else 4)
-    fc2_in = R_ * wl.I * (2 if wl.mode == "w4a16" else (1 + 1 / 32 if wl.mode == "mxfp8" else 0.5 + 1 / 16))
-    fc2_out = R_ * wl.H * 4
-    bytes_fc1 = wb1 + x_in + fc1_out
-    bytes_fc2 = wb2 + fc2_in + fc2_out
-    flops_fc1 = 2.0 * R_ * wl.N1 * wl.H
-    flops_fc2 = 2.0 * R_ * wl.H * wl.I
-    ms_det, ms_eager, st_det, pct_det = results[True] if True in results else results[False]
-    kernel = "fc1" if st_det["fc1"] >= st_det["fc2"] else "fc2"
-    kms = st_det[kernel]
-    kbytes = bytes_fc1 if kernel == "fc1" else bytes_fc2
-    kflops = flops_fc1 if kernel == "fc1" else flops_fc2
+    touched = int((counts > 0).sum())
+    b1, b2 = weight_bytes(d, wl.wfmt)
+    conf = "fused" if wl.finalize == ("fused",) else "det"   # the configured variant
+    other = "det" if conf == "fused" else "fused"
     decode = wl.T <= 1024
-    dtype = {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "mxfp8": "fp8"}[wl.mode]
-    if decode:
-        ach = kbytes / (kms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
-    else:
-        ach = kflops / (kms * 1e-3) / 1e12
-        peak = MFMA_PEAK_TFLOPS[dtype]
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4)}
-    tr = committed_traffic(wl.name, kernel)
-    roof["traffic"] = tr
-    roof["kernel"] = f"gemm_kernel ({kernel.upper()})"
-    roof["avg_launch_us"] = round(kms * 1e3, 2)
-    roof["algorithmic_bytes"] = int(kbytes)
-    roof["algorithmic_flops"] = kflops
-
-    out = {
-        "metric": METRIC,
-        "value": round(wl.T / (ms_det * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_det, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E,
-                   "K": wl.K, "mode": wl.mode, "act": wl.act,
-                   "router_weight_on_input": wl.on_input,
-                   "finalize": "deterministic" if True in results else "fused",
+    R_ = wl.T * wl.K
+    flops = 2.0 * R_ * (wl.N1 * wl.H + wl.H * wl.I)
+    v = variants[conf]
+    rec = {
+        "value": round(wl.T / (v["ms"] * 1e-3), 1),
+        "ms_per_step": round(v["ms"], 5),
+        "dtype": {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "mxfp8": "fp8"}[wl.mode],
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
+                   "mode": wl.mode, "act": wl.act, "router_weight_on_input": wl.on_input,
+                   "finalize": "fused" if conf == "fused" else "deterministic",
                    "timing": "hipGraph replay of one forward per step",
                    "weight_copies_rotated": copies, "touched_experts": touched,
                    "routing": routing_summary(counts)},
-        "eager_ms_per_step": round(ms_eager, 5),
-        "graph_step_ms_percentiles": pct_det,
-        "stages_us": {k: round(v * 1e3, 2) for k, v in st_det.items()},
-        "layer_tflops": round((flops_fc1 + flops_fc2) / (ms_det * 1e-3) / 1e12, 2),
-        "layer_weight_gbs": round((wb1 + wb2) / (ms_det * 1e-3) / 1e9, 1),
-        "roofline": roof,
+        "graph_step_ms_percentiles": v["pct"],
+        "stages_us": {k: round(u, 2) for k, u in v["st_us"].items()},
+        "layer_tflops": round(flops / (v["ms"] * 1e-3) / 1e12, 2),
+        "layer_weight_gbs": round(touched * (b1 + b2) / (v["ms"] * 1e-3) / 1e9, 1),
+        "roofline": roofline(wl, d, counts, v["st_us"], decode),
     }
-    if False in results and True in results:
-        ms_f, ms_fe, st_f, pct_f = results[False]
-        out["fused_finalize"] = {"value": round(wl.T / (ms_f * 1e-3), 1),
-                                 "ms_per_step": round(ms_f, 5),
-                                 "graph_step_ms_percentiles": pct_f,
-                                 "eager_ms_per_step": round(ms_fe, 5),
-                                 "stages_us": {k: round(v * 1e3, 2) for k, v in st_f.items()}}
-    out["cpu_baseline"] = None
+    o = variants[other]
+    rec["deterministic_finalize" if other == "det" else "fused_finalize"] = {
+        "value": round(wl.T / (o["ms"] * 1e-3), 1), "ms_per_step": round(o["ms"], 5),
+        "graph_step_ms_percentiles": o["pct"],
+        "stages_us": {k: round(u, 2) for k, u in o["st_us"].items()},
+        "roofline": roofline(wl, d, counts, o["st_us"], decode)}
+    rec["cpu_baseline"] = None
     if cpu_w is not None:
-        out["cpu_baseline"] = cpu_baseline(wl, x, logits, cpu_w[0], cpu_w[1],
-                                           args.cpu_sample_tokens)
+        n = args.cpu_sample_tokens or CPU_SAMPLE_TOKENS.get(wl.name, 8)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, logits, cpu_w[0], cpu_w[1], n)
+    del blobs, ws, y, x, logits
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs all experts on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+    torch.cuda.set_device(0)
+    head = run_workload(args.workload, args, not args.no_cpu_baseline)
+    out = {"metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": head["dtype"], "data": "synthetic"}
+    for k, v in head.items():
+        if k not in out:
+            out[k] = v
+    if not args.no_subrecords:
+        out["workloads"] = {}
+        for name in SUBRECORDS:
+            if name == args.workload:
+                continue
+            print(f"# sub-record {name}", file=sys.stderr, flush=True)
+            out["workloads"][name] = run_workload(name, args, False)
     print(json.dumps(out))
 
 

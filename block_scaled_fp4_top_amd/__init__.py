@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
-MODES = {"w4a4_tensor": 0, "w4a4_token": 1, "w4a16": 2, "mxfp8": 3}
+MODES = {"w4a4_tensor": 0, "w4a4_token": 1, "w4a16": 2, "mxfp8": 3, "w4a4_token_4o6": 4}
 ACTS = {"swiglu": 0, "relu2": 1}
 WFMTS = {"nvfp4": 0, "mxfp8": 1}
 VIEWS = {"topk_ids": 0, "topk_w": 1, "counts": 2, "offsets": 3, "row_to_route": 4,
@@ -49,7 +49,8 @@ def _load():
         "moe_prepare_weights": (ctypes.c_int, [D, P, P, P, sz, P]),
         "moe_check_prepared": (ctypes.c_int, [D, P, P]),
         "moe_workspace_bytes": (sz, [D, i32, i32, i32]),
-        "moe_forward": (ctypes.c_int, [D, P, P, P, i32, i32, i32, i32, i32, i32, P, sz, P, P]),
+        "moe_forward": (ctypes.c_int, [D, P, sz, P, P, i32, i32, i32, i32, i32, i32, P, sz, P, P]),
+        "moe_forward_status": (ctypes.c_int, [P, ctypes.POINTER(i32), P]),
         "moe_finalize": (ctypes.c_int, [P, i32, P, P, i32, i32, i32, P, P]),
         "moe_quantize": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P, P]),
         "moe_workspace_view": (ctypes.c_int, [D, i32, i32, i32, i32, ctypes.POINTER(sz),
@@ -67,7 +68,7 @@ def _load():
 
 _lib = _load()
 EXPORTS = ["moe_prepared_bytes", "moe_prepare_weights", "moe_check_prepared",
-           "moe_workspace_bytes", "moe_forward", "moe_finalize", "moe_quantize",
+           "moe_workspace_bytes", "moe_forward", "moe_forward_status", "moe_finalize", "moe_quantize",
            "moe_workspace_view", "moe_stage_timing", "moe_stage_times", "moe_last_error"]
 
 
@@ -167,6 +168,9 @@ def forward(d: Dims, blob: torch.Tensor, x: torch.Tensor, logits: torch.Tensor, 
     T = x.shape[0]
     _need(logits, "router_logits", torch.float32, (T, d.E), x.device)
     _need(blob, "prepared", torch.uint8, device=x.device)
+    if blob.numel() < prepared_bytes(d):
+        raise MoeError(3, f"prepared blob has {blob.numel()} bytes, {prepared_bytes(d)} needed "
+                          "for these dimensions")
     if workspace is None:
         workspace = torch.empty(workspace_bytes(d, T, K, mode), dtype=torch.uint8,
                                 device=x.device)
@@ -174,11 +178,21 @@ def forward(d: Dims, blob: torch.Tensor, x: torch.Tensor, logits: torch.Tensor, 
     if out is None:
         out = torch.empty((T, d.H), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, (T, d.H), x.device)
-    _check(_lib.moe_forward(ctypes.byref(d.c()), _ptr(blob), _ptr(x), _ptr(logits), T, K,
+    _check(_lib.moe_forward(ctypes.byref(d.c()), _ptr(blob), blob.numel(), _ptr(x), _ptr(logits), T, K,
                             MODES[mode], ACTS[d.act], int(bool(router_weight_on_input)),
                             int(bool(deterministic)), _ptr(workspace), workspace.numel(),
                             _ptr(out), ctypes.c_void_p(_stream(stream))))
     return out
+
+
+def forward_status(workspace: torch.Tensor, stream=None) -> int:
+    """Status word of the last forward on `workspace` (synchronises): 0, or
+    MOE_ERR_INVALID (1) when the blob's header did not match the call."""
+    _need(workspace, "workspace", torch.uint8)
+    st = ctypes.c_int32(-1)
+    _check(_lib.moe_forward_status(_ptr(workspace), ctypes.byref(st),
+                                   ctypes.c_void_p(_stream(stream))))
+    return st.value
 
 
 def finalize(permuted_out: torch.Tensor, route_to_row: torch.Tensor, weights, T: int, K: int,
@@ -204,11 +218,11 @@ def finalize(permuted_out: torch.Tensor, route_to_row: torch.Tensor, weights, T:
 
 def quantize(v: torch.Tensor, kind: str, stream=None):
     """Block-quantize an fp32 [rows, cols] matrix. kind: "nvfp4_tensor",
-    "nvfp4_row" or "mxfp8". Returns (codes, scales, g) as uint8/uint8/fp32
+    "nvfp4_row", "mxfp8" or "nvfp4_row_4o6". Returns (codes, scales, g) as uint8/uint8/fp32
     tensors (g is None for MXFP8)."""
     _need(v, "v", torch.float32)
     rows, cols = v.shape
-    k = {"nvfp4_tensor": 0, "nvfp4_row": 1, "mxfp8": 2}[kind]
+    k = {"nvfp4_tensor": 0, "nvfp4_row": 1, "mxfp8": 2, "nvfp4_row_4o6": 3}[kind]
     dev = v.device
     if k == 2:
         codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)

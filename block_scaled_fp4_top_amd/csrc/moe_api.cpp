@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -30,6 +31,11 @@ static int fail(int code, const char* fmt, ...) {
     g_err = buf;
     return code;
 }
+
+namespace moe {
+// The same error reporting for the other translation units of the library.
+int report_error(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace moe
 
 static int hip_fail(hipError_t e, const char* where) {
     return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
@@ -119,7 +125,8 @@ extern "C" int moe_check_prepared(const moe_dims* d, const void* prepared, hipSt
 }
 
 static int check_mode(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
-    if (mode < MOE_W4A4_TENSOR || mode > MOE_MXFP8) return fail(MOE_ERR_INVALID, "mode=%d is not a moe_mode", mode);
+    if (mode < MOE_W4A4_TENSOR || mode > MOE_W4A4_TOKEN_4O6)
+        return fail(MOE_ERR_INVALID, "mode=%d is not a moe_mode", mode);
     if (T < 1) return fail(MOE_ERR_INVALID, "T=%d must be >= 1", T);
     if (K < 1 || K > d->E || K > kMaxK) return fail(MOE_ERR_INVALID, "K=%d outside [1, min(E=%d, %d)]", K, d->E, kMaxK);
     if ((long long)T * K > (1LL << 30)) return fail(MOE_ERR_UNSUPPORTED, "T*K=%lld too large", (long long)T * K);
@@ -163,16 +170,18 @@ extern "C" int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32
 namespace {
 constexpr int kStages = 7;
 constexpr int kRing = 128;
+// All timer state is touched only with `mu` held: a forward holds it from its
+// first to its last event while timing is on (so forwards on several host
+// threads serialise then), moe_stage_times while it drains.
 struct StageTimer {
     std::mutex mu;
-    bool enabled = false;
+    std::atomic<bool> enabled{false};
     bool init = false;
     hipEvent_t ev[kRing][kStages + 1];
     bool used[kRing][kStages + 1];
     int head = 0, pending = 0;
     double sum_ms[kStages] = {0};
     int forwards = 0;
-    int cur = -1;
 };
 StageTimer g_timer;
 
@@ -192,47 +201,48 @@ void timer_drain_one(int slot) {
     T.forwards++;
 }
 
-void timer_begin(hipStream_t s) {
+// Takes a ring slot for one forward (the caller holds mu and timing is on).
+int timer_begin() {
     StageTimer& T = g_timer;
-    if (!T.enabled) { T.cur = -1; return; }
     if (!T.init) {
         for (int i = 0; i < kRing; ++i)
             for (int j = 0; j <= kStages; ++j) (void)hipEventCreate(&T.ev[i][j]);
         T.init = true;
     }
-    if (T.pending == kRing) {  // ring full: account the oldest forward
+    if (T.pending == kRing) {  // ring full: account the oldest forward (waits for its events)
         timer_drain_one((T.head - T.pending + kRing) % kRing);
         T.pending--;
     }
-    T.cur = T.head;
+    const int slot = T.head;
     T.head = (T.head + 1) % kRing;
     T.pending++;
-    for (int j = 0; j <= kStages; ++j) T.used[T.cur][j] = false;
-    (void)s;
+    for (int j = 0; j <= kStages; ++j) T.used[slot][j] = false;
+    return slot;
 }
 
 // Events recorded by a kernel launch itself (its start and end) for the
-// boundaries `stage` and `stage + 1`; null when timing is off.
-void timer_kernel_events(int stage, hipEvent_t* t0, hipEvent_t* t1) {
+// boundaries `stage` and `stage + 1`; null when the forward is not timed
+// (slot < 0).
+void timer_kernel_events(int slot, int stage, hipEvent_t* t0, hipEvent_t* t1) {
     StageTimer& T = g_timer;
     *t0 = *t1 = nullptr;
-    if (T.cur < 0) return;
-    *t0 = T.ev[T.cur][stage];
-    *t1 = T.ev[T.cur][stage + 1];
-    T.used[T.cur][stage] = T.used[T.cur][stage + 1] = true;
+    if (slot < 0) return;
+    *t0 = T.ev[slot][stage];
+    *t1 = T.ev[slot][stage + 1];
+    T.used[slot][stage] = T.used[slot][stage + 1] = true;
 }
 
-void timer_mark(int stage, hipStream_t s) {
+void timer_mark(int slot, int stage, hipStream_t s) {
     StageTimer& T = g_timer;
-    if (T.cur < 0) return;
-    (void)hipEventRecord(T.ev[T.cur][stage], s);
-    T.used[T.cur][stage] = true;
+    if (slot < 0) return;
+    (void)hipEventRecord(T.ev[slot][stage], s);
+    T.used[slot][stage] = true;
 }
 }  // namespace
 
 extern "C" int moe_stage_timing(int32_t enable) {
     std::lock_guard<std::mutex> lk(g_timer.mu);
-    g_timer.enabled = enable != 0;
+    g_timer.enabled.store(enable != 0);
     return MOE_OK;
 }
 
@@ -261,29 +271,79 @@ static int pick_bm_index(long long R, int E) {
     return 3;
 }
 
-extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
-                           const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
-                           int32_t router_weight_on_input, int32_t deterministic_finalize,
-                           void* workspace, size_t workspace_bytes, uint16_t* y,
-                           hipStream_t stream) {
+// Every check of a forward's arguments except the workspace's (all before any
+// launch).
+static int check_forward_args(const moe_dims* d, const void* prepared, size_t prepared_bytes,
+                              const uint16_t* x, const float* logits, int32_t T, int32_t K,
+                              int32_t mode, int32_t act, int32_t router_weight_on_input,
+                              int32_t deterministic_finalize, const uint16_t* y) {
     int rc = check_dims(d);
     if (rc) return rc;
     rc = check_mode(d, T, K, mode);
     if (rc) return rc;
     if (act != d->act) return fail(MOE_ERR_INVALID, "act=%d differs from the prepared act=%d", act, d->act);
-    if (!prepared || !x || !logits || !workspace || !y) return fail(MOE_ERR_INVALID, "NULL pointer argument");
-    if (!aligned(prepared, 256) || !aligned(workspace, 256))
-        return fail(MOE_ERR_INVALID, "prepared and workspace must be 256-byte aligned");
+    if (!prepared || !x || !logits || !y) return fail(MOE_ERR_INVALID, "NULL pointer argument");
+    BlobLayout L0;
+    make_blob_layout(*d, &L0);
+    if (prepared_bytes < L0.h.total)
+        return fail(MOE_ERR_WORKSPACE, "prepared blob %zu bytes < %llu for these dimensions",
+                    prepared_bytes, (unsigned long long)L0.h.total);
+    if (!aligned(prepared, 256)) return fail(MOE_ERR_INVALID, "prepared must be 256-byte aligned");
     if (!aligned(x, 16) || !aligned(logits, 16) || !aligned(y, 16))
         return fail(MOE_ERR_INVALID, "x, logits and y must be 16-byte aligned");
     if (router_weight_on_input != 0 && router_weight_on_input != 1)
         return fail(MOE_ERR_INVALID, "router_weight_on_input must be 0 or 1");
     if (deterministic_finalize != 0 && deterministic_finalize != 1)
         return fail(MOE_ERR_INVALID, "deterministic_finalize must be 0 or 1");
+    return MOE_OK;
+}
+
+namespace moe {
+// Bytes of workspace a forward of this shape uses (arguments already checked).
+size_t forward_workspace_bytes(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
     WsPlan P;
     plan_workspace(*d, T, K, mode, &P);
-    if (workspace_bytes < P.total)
-        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, P.total);
+    return P.total;
+}
+
+int forward_checked(const moe_dims* d, const void* prepared, size_t prepared_bytes,
+                    const uint16_t* x, const float* logits, int32_t T, int32_t K, int32_t mode,
+                    int32_t act, int32_t router_weight_on_input, int32_t deterministic_finalize,
+                    const uint16_t* y) {
+    return check_forward_args(d, prepared, prepared_bytes, x, logits, T, K, mode, act,
+                              router_weight_on_input, deterministic_finalize, y);
+}
+int enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
+                    const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
+                    int32_t router_weight_on_input, int32_t deterministic_finalize,
+                    void* workspace, uint16_t* y, hipStream_t stream);
+}  // namespace moe
+
+extern "C" int moe_forward(const moe_dims* d, const void* prepared, size_t prepared_bytes,
+                           const uint16_t* x, const float* logits, int32_t T, int32_t K,
+                           int32_t mode, int32_t act, int32_t router_weight_on_input,
+                           int32_t deterministic_finalize, void* workspace,
+                           size_t workspace_bytes, uint16_t* y, hipStream_t stream) {
+    int rc = check_forward_args(d, prepared, prepared_bytes, x, logits, T, K, mode, act,
+                                router_weight_on_input, deterministic_finalize, y);
+    if (rc) return rc;
+    if (!workspace) return fail(MOE_ERR_INVALID, "NULL workspace");
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace must be 256-byte aligned");
+    const size_t need = forward_workspace_bytes(d, T, K, mode);
+    if (workspace_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    return enqueue_forward(d, prepared, x, logits, T, K, mode, act, router_weight_on_input,
+                           deterministic_finalize, workspace, y, stream);
+}
+
+// The launch sequence of one forward; every argument has been checked and
+// `workspace` holds at least forward_workspace_bytes(d, T, K, mode) bytes.
+int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
+                         const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
+                         int32_t router_weight_on_input, int32_t deterministic_finalize,
+                         void* workspace, uint16_t* y, hipStream_t stream) {
+    WsPlan P;
+    plan_workspace(*d, T, K, mode, &P);
 
     BlobLayout L;
     make_blob_layout(*d, &L);
@@ -301,15 +361,20 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     int32_t* bhist = WS(int32_t, V_BHIST);
     int32_t* bbase = bhist + (size_t)P.nblk * E;
     uint32_t* misc = WS(uint32_t, V_MISC);
-    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN;
+    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
     const bool f8 = mode == MOE_MXFP8;
-    const bool per_row = mode == MOE_W4A4_TOKEN;
+    const bool per_row = mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
+    const int qkind = mode == MOE_W4A4_TOKEN_4O6 ? QK_NV_ROW_4O6 : (per_row ? QK_NV_ROW : QK_NV_TENSOR);
     const bool fused = deterministic_finalize == 0;
+    uint32_t* status = reinterpret_cast<uint32_t*>(ws);
 
-    timer_begin(stream);
-    timer_mark(0, stream);
-    HIP_TRY(launch_route(logits, T, E, K, ids, topw, misc, stream), "route");
-    timer_mark(1, stream);
+    // while stage timing is on, the timer state belongs to this forward
+    std::unique_lock<std::mutex> timing_lock(g_timer.mu, std::defer_lock);
+    if (g_timer.enabled.load()) timing_lock.lock();
+    const int tslot = timing_lock.owns_lock() && g_timer.enabled.load() ? timer_begin() : -1;
+    timer_mark(tslot, 0, stream);
+    HIP_TRY(launch_route(logits, T, E, K, ids, topw, misc, blob, L.h, status, stream), "route");
+    timer_mark(tslot, 1, stream);
     if (small_route_permute(R, E)) {
         HIP_TRY(launch_permute_small(ids, R, E, counts, offsets, tiles, r2r, rt2row, stream), "permute");
     } else {
@@ -317,12 +382,12 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
                                stream),
                 "permute");
     }
-    timer_mark(2, stream);
+    timer_mark(tslot, 2, stream);
     if (nv4) {
         if (!per_row)
             HIP_TRY(launch_amax(x, 1, (size_t)T * H, misc + kMiscXAmax, kAmaxSlots, kAmaxStride, stream),
                     "x amax");
-        HIP_TRY(launch_quant_rows(x, 1, T, H, per_row ? QK_NV_ROW : QK_NV_TENSOR, misc + kMiscXAmax, kAmaxSlots, kAmaxStride,
+        HIP_TRY(launch_quant_rows(x, 1, T, H, qkind, misc + kMiscXAmax, kAmaxSlots, kAmaxStride,
                                   WS(uint8_t, V_XCODES), WS(uint8_t, V_XSCALES), WS(float, V_XG),
                                   WS(uint16_t, V_XDEQ), stream),
                 "quantize x");
@@ -369,12 +434,13 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
         g1.out_bf16 = WS(uint16_t, V_A2F);
     }
     g1.amax_slot = mode == MOE_W4A4_TENSOR ? misc + kMiscA2Amax : nullptr;
+    g1.status = status;
     hipEvent_t t0, t1;
-    timer_kernel_events(3, &t0, &t1);
+    timer_kernel_events(tslot, 3, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC1, bmi, g1, stream, t0, t1), "FC1");
 
     if (nv4) {
-        HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, per_row ? QK_NV_ROW : QK_NV_TENSOR,
+        HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, qkind,
                                   misc + kMiscA2Amax, kAmaxSlots, kAmaxStride, WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES),
                                   WS(float, V_A2G), WS(uint16_t, V_A2DEQ), stream),
                 "quantize FC2 input");
@@ -409,18 +475,29 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, const uint16
     // a token accumulator well above the 256 MB last-level cache: N-block-major
     // FC2 order, so each phase's atomics stay in cache
     g2.phased = fused && (size_t)T * H * 4 > kPhasedYaccBytes;
-    timer_kernel_events(5, &t0, &t1);
+    g2.status = status;
+    timer_kernel_events(tslot, 5, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream, t0, t1), "FC2");
 
     if (fused) {
-        HIP_TRY(launch_yacc_to_bf16(WS(float, V_YACC), (size_t)T * H, y, stream), "convert y");
+        HIP_TRY(launch_yacc_to_bf16(WS(float, V_YACC), (size_t)T * H, y, status, stream), "convert y");
     } else {
         HIP_TRY(launch_finalize(WS(float, V_O), 0, rt2row, router_weight_on_input ? nullptr : topw, T, K, H,
-                                y, stream),
+                                y, status, stream),
                 "finalize");
     }
-    timer_mark(7, stream);
+    timer_mark(tslot, 7, stream);
 #undef WS
+    return MOE_OK;
+}
+
+extern "C" int moe_forward_status(const void* workspace, int32_t* status, hipStream_t stream) {
+    if (!workspace || !status) return fail(MOE_ERR_INVALID, "NULL pointer argument");
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID, "workspace must be 256-byte aligned");
+    uint32_t w = 0;
+    HIP_TRY(hipMemcpyAsync(&w, workspace, sizeof w, hipMemcpyDeviceToHost, stream), "read status");
+    HIP_TRY(hipStreamSynchronize(stream), "sync");
+    *status = (int32_t)w;
     return MOE_OK;
 }
 
@@ -434,20 +511,21 @@ extern "C" int moe_finalize(const void* permuted_out, int32_t out_is_bf16, const
     if (!aligned(permuted_out, 16) || !aligned(y, 16) || !aligned(route_to_row, 4) ||
         (weights && !aligned(weights, 4)))
         return fail(MOE_ERR_INVALID, "misaligned pointer");
-    HIP_TRY(launch_finalize(permuted_out, out_is_bf16, route_to_row, weights, T, K, H, y, stream), "finalize");
+    HIP_TRY(launch_finalize(permuted_out, out_is_bf16, route_to_row, weights, T, K, H, y, nullptr, stream),
+            "finalize");
     return MOE_OK;
 }
 
 extern "C" int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8_t* codes,
                             uint8_t* scales, float* g, void* scratch, hipStream_t stream) {
     if (!v || !codes || !scales || !scratch) return fail(MOE_ERR_INVALID, "NULL pointer argument");
-    if (kind < 0 || kind > 2) return fail(MOE_ERR_INVALID, "kind=%d invalid", kind);
+    if (kind < 0 || kind > 3) return fail(MOE_ERR_INVALID, "kind=%d invalid", kind);
     if (kind != 2 && !g) return fail(MOE_ERR_INVALID, "g is NULL for NVFP4");
     if (rows < 1 || cols < 32 || cols % 32) return fail(MOE_ERR_UNSUPPORTED, "rows=%d cols=%d unsupported", rows, cols);
     if (!aligned(v, 16) || !aligned(codes, 16) || !aligned(scratch, 4))
         return fail(MOE_ERR_INVALID, "misaligned pointer");
     uint32_t* slot = static_cast<uint32_t*>(scratch);
-    const int qk = kind == 0 ? QK_NV_TENSOR : (kind == 1 ? QK_NV_ROW : QK_MX);
+    const int qk = kind == 0 ? QK_NV_TENSOR : (kind == 1 ? QK_NV_ROW : (kind == 2 ? QK_MX : QK_NV_ROW_4O6));
     if (qk == QK_NV_TENSOR) {
         HIP_TRY(launch_fill_u32(slot, 1, 0u, stream), "clear scratch");
         HIP_TRY(launch_amax(v, 0, (size_t)rows * cols, slot, 1, 1, stream), "amax");

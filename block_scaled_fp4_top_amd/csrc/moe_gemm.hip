@@ -243,6 +243,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
+    // the forward's status word, loaded here and tested after the tile lookup
+    // so that its latency overlaps the lookup's loads
+    const uint32_t status = p.status ? *p.status : 0u;
     // Block order. Blocks are dealt round-robin over the 8 XCDs (each with its
     // own L2) and the grid is a multiple of 8, so blockIdx % 8 names the XCD.
     //  - Wide tiles: M-tile fastest (across experts), then N-block, in
@@ -313,6 +316,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     const int mt_local = mt - p.tiles[e];
     const int row0 = p.offsets[e] + mt_local * BM;
     const int rows = min(BM, p.offsets[e + 1] - row0);
+    if (status) return;  // blob prepared for other dimensions: no weight reads, no stores
     for (int m = tid; m < BM; m += NW * 64)
         s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
     __syncthreads();

@@ -113,6 +113,12 @@ constexpr int kMiscWords = 2 * kAmaxSlots * kAmaxStride;
 // accumulator T x H exceeds this (half the 256 MB last-level cache).
 constexpr size_t kPhasedYaccBytes = 128ull << 20;
 
+// The first kWsStatusBytes of a forward's workspace hold its status word:
+// the routing kernel writes 0, or MOE_ERR_INVALID when the prepared blob's
+// header does not match the dimensions of the call; the kernels that read the
+// weights or write the output skip their work when it is not 0.
+constexpr size_t kWsStatusBytes = 256;
+
 enum WsView {
     V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
@@ -129,7 +135,7 @@ struct WsPlan {
 
 inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p) {
     const size_t R = (size_t)T * K, E = (size_t)d.E, H = (size_t)d.H, I = (size_t)d.I;
-    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN;
+    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
     const bool f8 = mode == MOE_MXFP8;
     p->nblk = (int)((R + kPermChunk - 1) / kPermChunk);
     for (int v = 0; v < V_NUM; ++v) p->bytes[v] = 0;
@@ -163,7 +169,7 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
     }
     p->bytes[V_O] = R * H * 4;
     p->bytes[V_YACC] = (size_t)T * H * 4;
-    size_t off = 0;
+    size_t off = kWsStatusBytes;
     for (int v = 0; v < V_NUM; ++v) {
         p->off[v] = off;
         off = align256(off + p->bytes[v]);
@@ -294,6 +300,83 @@ __device__ __forceinline__ void nvfp4_block(const float* v, float g, uint32_t* p
     packed[0] = w0;
     packed[1] = w1;
     *sf_out = sf;
+}
+
+// One NVFP4 candidate for a 16-element block with block max `ab` mapped to
+// `top` (6: the usual mapping, 4: the alternative of the 4-over-6 choice):
+// s = ab / (top g), sf = E4M3(s), d = float(sf) g, codes E2M1(v / d), each one
+// IEEE fp32 operation in this order (d == 0: sign-only codes). Returns the
+// block's sum of squared errors sum_i (v_i - code_i d)^2, accumulated in fp64
+// in element order with every operation rounded once (no contraction), so the
+// choice between candidates is reproducible bit for bit.
+__device__ __forceinline__ double nvfp4_candidate(const float* v, float g, float ab, float top,
+                                                  uint32_t* packed, uint32_t* sf_out) {
+    const uint32_t sf = e4m3_code(__fdiv_rn(ab, __fmul_rn(top, g)));
+    const float d = __fmul_rn(e4m3_value(sf), g);
+    uint32_t w0 = 0, w1 = 0;
+    if (d != 0.0f) {
+        float u[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) u[i] = __fdiv_rn(v[i], d);
+        w0 = e2m1_pair<0>(w0, u[0], u[1]);
+        w0 = e2m1_pair<1>(w0, u[2], u[3]);
+        w0 = e2m1_pair<2>(w0, u[4], u[5]);
+        w0 = e2m1_pair<3>(w0, u[6], u[7]);
+        w1 = e2m1_pair<0>(w1, u[8], u[9]);
+        w1 = e2m1_pair<1>(w1, u[10], u[11]);
+        w1 = e2m1_pair<2>(w1, u[12], u[13]);
+        w1 = e2m1_pair<3>(w1, u[14], u[15]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t c = (f2u(v[i]) >> 28) & 8u;
+            if (i < 8) w0 |= c << (4 * i); else w1 |= c << (4 * (i - 8));
+        }
+    }
+    float c[16];
+    e2m1x8_to_f32(w0, c);
+    e2m1x8_to_f32(w1, c + 8);
+    double e = 0.0;
+    const double dd = (double)d;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const double diff = __dsub_rn((double)v[i], __dmul_rn((double)c[i], dd));
+        e = __dadd_rn(e, __dmul_rn(diff, diff));
+    }
+    packed[0] = w0;
+    packed[1] = w1;
+    *sf_out = sf;
+    return e;
+}
+
+// NVFP4 "4-over-6" quantization of one 16-element block with the global scale
+// g = amax / (6 * 256) of its row: the max-to-6 and the max-to-4 candidates,
+// and the one with the smaller squared error (ties to max-to-6). g == 0 gives
+// scale 0 and sign-only codes.
+__device__ __forceinline__ void nvfp4_block_4o6(const float* v, float g, uint32_t* packed,
+                                                uint32_t* sf_out) {
+    if (g == 0.0f) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t c = (f2u(v[i]) >> 28) & 8u;
+            if (i < 8) w0 |= c << (4 * i); else w1 |= c << (4 * (i - 8));
+        }
+        packed[0] = w0;
+        packed[1] = w1;
+        *sf_out = 0;
+        return;
+    }
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ab = fmaxf(ab, fabsf(v[i]));
+    uint32_t p6[2], s6, p4[2], s4;
+    const double e6 = nvfp4_candidate(v, g, ab, 6.0f, p6, &s6);
+    const double e4 = nvfp4_candidate(v, g, ab, 4.0f, p4, &s4);
+    const bool four = e4 < e6;
+    packed[0] = four ? p4[0] : p6[0];
+    packed[1] = four ? p4[1] : p6[1];
+    *sf_out = four ? s4 : s6;
 }
 
 // MXFP8 quantization of one 32-element block (OCP MX v1.0 scale rule):

@@ -3,12 +3,19 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/moe_fp4.h"
 
 namespace moe {
 
+struct BlobHeader;
+// Routing; block 0 also clears `misc` and writes the forward's status word
+// (0, or MOE_ERR_INVALID when the blob's header differs from `expect`).
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
-                        uint32_t* misc, hipStream_t s);
+                        uint32_t* misc, const void* blob, const BlobHeader& expect,
+                        uint32_t* status, hipStream_t s);
 bool small_route_permute(int R, int E);
 hipError_t launch_permute_small(const int32_t* ids, int R, int E, int32_t* counts,
                                 int32_t* offsets, int32_t* tiles, int32_t* r2r, int32_t* rt2row,
@@ -22,7 +29,9 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int nblk, int32_t* b
 // non-negative partial maximum), 1 NVFP4 one global scale per row, 2 MXFP8. in_bf16: input
 // rows are bf16 (else fp32). deq (NVFP4 only, may be null): fp16 [rows][cols]
 // of code * sf.
-enum QuantKind { QK_NV_TENSOR = 0, QK_NV_ROW = 1, QK_MX = 2 };
+// QK_NV_ROW_4O6: one global scale amax / (6 * 256) per row and the 4-over-6
+// block choice (nvfp4_block_4o6).
+enum QuantKind { QK_NV_TENSOR = 0, QK_NV_ROW = 1, QK_MX = 2, QK_NV_ROW_4O6 = 3 };
 // Max |v| into the nslots words stride apart from amax_slot (already cleared).
 hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* amax_slot, int nslots,
                        int stride, hipStream_t s);
@@ -31,9 +40,12 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
                              uint8_t* scales, float* g, uint16_t* deq, hipStream_t s);
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
-hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, hipStream_t s);
+// status: the forward's status word (skip all work when not 0), or null.
+hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, const uint32_t* status,
+                               hipStream_t s);
 hipError_t launch_finalize(const void* O, int is_bf16, const int32_t* rt2row, const float* w,
-                           int T, int K, int H, uint16_t* y, hipStream_t s);
+                           int T, int K, int H, uint16_t* y, const uint32_t* status,
+                           hipStream_t s);
 
 // Weight preparation (one matrix family W[E][N][K] at a time).
 hipError_t launch_prep_amax(const float* w, int E, size_t per_expert, uint32_t* amax, hipStream_t s);
@@ -78,7 +90,22 @@ struct GemmArgs {
     float* yacc;         // FC2 fused: [T][N]
     int fused;
     int phased;          // FC2 fused on wide tiles: N-block-major block order (large y_acc)
+    const uint32_t* status;  // the forward's status word: blocks exit when it is not 0
 };
+
+// The forward as the C ABI runs it (moe_api.cpp): argument checks other than
+// the workspace's, the workspace a shape needs, and the launch sequence on a
+// workspace of at least that size. report_error sets moe_last_error().
+int forward_checked(const moe_dims* d, const void* prepared, size_t prepared_bytes,
+                    const uint16_t* x, const float* logits, int32_t T, int32_t K, int32_t mode,
+                    int32_t act, int32_t router_weight_on_input, int32_t deterministic_finalize,
+                    const uint16_t* y);
+size_t forward_workspace_bytes(const moe_dims* d, int32_t T, int32_t K, int32_t mode);
+int enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
+                    const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
+                    int32_t router_weight_on_input, int32_t deterministic_finalize,
+                    void* workspace, uint16_t* y, hipStream_t stream);
+int report_error(int code, const char* msg);
 
 // t0/t1: optional events recorded at the kernel's start and end.
 hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStream_t s,

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
             __syncthreads();
             m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
         }
-        gg = __fdiv_rn(m, 2688.0f);
+        gg = __fdiv_rn(m, KIND == QK_NV_ROW_4O6 ? 1536.0f : 2688.0f);
         if (lt == 0) g[row] = gg;
     }
     const int nb = cols / 16;
@@ -116,7 +116,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
         float vv[16];
         load16<BF16>(v, base + (size_t)b * 16, vv);
         uint32_t packed[2], sf;
-        nvfp4_block(vv, gg, packed, &sf);
+        if (KIND == QK_NV_ROW_4O6) nvfp4_block_4o6(vv, gg, packed, &sf);
+        else nvfp4_block(vv, gg, packed, &sf);
         *reinterpret_cast<uint2*>(codes + base / 2 + (size_t)b * 8) = make_uint2(packed[0], packed[1]);
         scales[(size_t)row * nb + b] = (uint8_t)sf;
         if (deq) {
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 // NVFP4 with one global scale per row, rows of at most 64 * 16 * NBL values:
 // one wave per row holds its row in registers (lane l owns the 16-element
 // blocks l, l + 64, ...), so the row max and the quantization read HBM once.
-template <bool BF16, int NBL>
+template <bool BF16, int NBL, bool F46>
 __global__ __launch_bounds__(256) void quant_rows_nvrow_kernel(const void* __restrict__ v, int rows,
                                                                int cols,
                                                                uint8_t* __restrict__ codes,
@@ -156,14 +157,15 @@ __global__ __launch_bounds__(256) void quant_rows_nvrow_kernel(const void* __res
         }
     }
     m = wave_max(m);
-    const float gg = __fdiv_rn(m, 2688.0f);
+    const float gg = __fdiv_rn(m, F46 ? 1536.0f : 2688.0f);
     if (lane == 0) g[row] = gg;
 #pragma unroll
     for (int j = 0; j < NBL; ++j) {
         const int b = lane + 64 * j;
         if (b >= nb) break;
         uint32_t packed[2], sf;
-        nvfp4_block(vv[j], gg, packed, &sf);
+        if (F46) nvfp4_block_4o6(vv[j], gg, packed, &sf);
+        else nvfp4_block(vv[j], gg, packed, &sf);
         *reinterpret_cast<uint2*>(codes + base / 2 + (size_t)b * 8) = make_uint2(packed[0], packed[1]);
         scales[(size_t)row * nb + b] = (uint8_t)sf;
         if (deq) {
@@ -215,7 +217,8 @@ typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
 // y = bf16(y_acc), four elements per thread and step; y_acc is read once, so
 // its loads are non-temporal.
 __global__ void yacc_to_bf16_kernel(const float* __restrict__ yacc, size_t n4,
-                                    uint16_t* __restrict__ y) {
+                                    uint16_t* __restrict__ y, const uint32_t* __restrict__ status) {
+    if (status && *status) return;
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
         const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(yacc) + i);
         reinterpret_cast<uint2*>(y)[i] =
@@ -234,14 +237,17 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const void* __restrict__ O,
                                                        const int32_t* __restrict__ rt2row,
                                                        const float* __restrict__ w, int K, int H,
-                                                       uint16_t* __restrict__ y) {
+                                                       uint16_t* __restrict__ y,
+                                                       const uint32_t* __restrict__ status) {
     __shared__ int32_t s_row[kMaxK];
     __shared__ float s_w[kMaxK];
     const int t = blockIdx.x;
+    const uint32_t st = status ? *status : 0u;  // issued beside the route loads
     if ((int)threadIdx.x < K) {
         s_row[threadIdx.x] = rt2row[(size_t)t * K + threadIdx.x];
         s_w[threadIdx.x] = w ? w[(size_t)t * K + threadIdx.x] : 1.0f;
     }
+    if (st) return;  // uniform over the block
     __syncthreads();
     const int c_end = gridDim.y == 1 ? H : min(H, ((int)blockIdx.y + 1) * 1024);
     for (int c = blockIdx.y * 1024 + threadIdx.x * 4; c < c_end; c += 1024) {
@@ -411,16 +417,19 @@ hipError_t launch_amax(const void* v, int in_bf16, size_t n, uint32_t* slot, int
 hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int kind,
                              const uint32_t* amax_slot, int amax_slots, int amax_stride, uint8_t* codes,
                              uint8_t* scales, float* g, uint16_t* deq, hipStream_t s) {
-    if (kind == QK_NV_ROW && !(rows < 2048 && cols >= 1024) && cols <= 64 * 16 * 8) {
+    const bool per_row = kind == QK_NV_ROW || kind == QK_NV_ROW_4O6;
+    if (per_row && !(rows < 2048 && cols >= 1024) && cols <= 64 * 16 * 8) {
         // single pass with the row in registers
         const int nbl = (cols / 16 + 63) / 64;
         const dim3 grid4((rows + 3) / 4), block4(256);
-#define QN(BF, N) hipLaunchKernelGGL((quant_rows_nvrow_kernel<BF, N>), grid4, block4, 0, s, v, rows, cols, codes, scales, g, deq)
+#define QN(BF, N, F) hipLaunchKernelGGL((quant_rows_nvrow_kernel<BF, N, F>), grid4, block4, 0, s, v, rows, cols, codes, scales, g, deq)
+#define QNB(BF, F) do { if (nbl <= 1) QN(BF, 1, F); else if (nbl <= 2) QN(BF, 2, F); else if (nbl <= 4) QN(BF, 4, F); else QN(BF, 8, F); } while (0)
         if (in_bf16) {
-            if (nbl <= 1) QN(true, 1); else if (nbl <= 2) QN(true, 2); else if (nbl <= 4) QN(true, 4); else QN(true, 8);
+            if (kind == QK_NV_ROW_4O6) QNB(true, true); else QNB(true, false);
         } else {
-            if (nbl <= 1) QN(false, 1); else if (nbl <= 2) QN(false, 2); else if (nbl <= 4) QN(false, 4); else QN(false, 8);
+            if (kind == QK_NV_ROW_4O6) QNB(false, true); else QNB(false, false);
         }
+#undef QNB
 #undef QN
         return hipGetLastError();
     }
@@ -428,17 +437,19 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
     // very few rows: also split each row (not for per-row scales, whose row
     // maximum needs the whole row in one block)
     const int qb = kind == QK_MX ? 32 : 16;
-    const unsigned chunks = (wide && rows < 256 && kind != QK_NV_ROW) ? (unsigned)((cols / qb + 255) / 256) : 1u;
+    const unsigned chunks = (wide && rows < 256 && !per_row) ? (unsigned)((cols / qb + 255) / 256) : 1u;
     const dim3 grid(wide ? rows : (rows + 3) / 4, chunks), block(256);
 #define QR(KD, BF, W) hipLaunchKernelGGL((quant_rows_kernel<KD, BF, W>), grid, block, 0, s, v, rows, cols, amax_slot, amax_slots, amax_stride, codes, scales, g, deq)
 #define QRW(KD, BF) do { if (wide) QR(KD, BF, 4); else QR(KD, BF, 1); } while (0)
     if (in_bf16) {
         if (kind == QK_NV_TENSOR) QRW(QK_NV_TENSOR, true);
         else if (kind == QK_NV_ROW) QRW(QK_NV_ROW, true);
+        else if (kind == QK_NV_ROW_4O6) QRW(QK_NV_ROW_4O6, true);
         else QRW(QK_MX, true);
     } else {
         if (kind == QK_NV_TENSOR) QRW(QK_NV_TENSOR, false);
         else if (kind == QK_NV_ROW) QRW(QK_NV_ROW, false);
+        else if (kind == QK_NV_ROW_4O6) QRW(QK_NV_ROW_4O6, false);
         else QRW(QK_MX, false);
     }
 #undef QRW
@@ -451,20 +462,23 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, hipStream_t s) {
+hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, const uint32_t* status,
+                               hipStream_t s) {
     // n = T * H is a multiple of 128 (H is)
-    hipLaunchKernelGGL(yacc_to_bf16_kernel, dim3(grid_for(n / 4, 8192)), dim3(256), 0, s, yacc, n / 4, y);
+    hipLaunchKernelGGL(yacc_to_bf16_kernel, dim3(grid_for(n / 4, 8192)), dim3(256), 0, s, yacc, n / 4, y,
+                       status);
     return hipGetLastError();
 }
 
 hipError_t launch_finalize(const void* O, int is_bf16, const int32_t* rt2row, const float* w,
-                           int T, int K, int H, uint16_t* y, hipStream_t s) {
+                           int T, int K, int H, uint16_t* y, const uint32_t* status,
+                           hipStream_t s) {
     // few tokens: one block per 1024 columns as well, so the reads of O keep
     // enough blocks in flight (64 tokens of 7168 columns: the finalize stage
     // went from 14 to 7 us)
     const dim3 grid(T, T < 2048 ? (H + 1023) / 1024 : 1);
-    if (is_bf16) hipLaunchKernelGGL(finalize_kernel<true>, grid, dim3(256), 0, s, O, rt2row, w, K, H, y);
-    else hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(256), 0, s, O, rt2row, w, K, H, y);
+    if (is_bf16) hipLaunchKernelGGL(finalize_kernel<true>, grid, dim3(256), 0, s, O, rt2row, w, K, H, y, status);
+    else hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(256), 0, s, O, rt2row, w, K, H, y, status);
     return hipGetLastError();
 }
 

@@ -94,13 +94,31 @@ __device__ __forceinline__ void route_one_token(const float* __restrict__ lt, in
 // rounds of a wave-wide (max value, min index) reduction pick the experts in
 // descending order with ties to the lower id. Lane k keeps the k-th pick.
 // p_k = exp(l_k - l_max) / sum_j exp(l_j - l_max), summed in k order.
+// Block 0 also clears the misc words of the forward and compares the
+// prepared blob's header with the one the call's dimensions imply (one word
+// per lane of its first wave): the status word becomes MOE_ERR_INVALID on any
+// difference, 0 otherwise, so the later kernels of the forward skip a blob
+// prepared for other dimensions, activation or format.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int K, int32_t* __restrict__ ids,
                                                          float* __restrict__ topw,
-                                                         uint32_t* __restrict__ misc) {
-    if (blockIdx.x == 0)
+                                                         uint32_t* __restrict__ misc,
+                                                         const uint32_t* __restrict__ blob,
+                                                         BlobHeader expect,
+                                                         uint32_t* __restrict__ status) {
+    if (blockIdx.x == 0) {
         for (int i = threadIdx.x; i < kMiscWords; i += blockDim.x) misc[i] = 0u;
+        if (threadIdx.x < 64) {
+            constexpr int kWords = sizeof(BlobHeader) / 4;
+            static_assert(kWords <= 64, "one header word per lane");
+            const uint32_t* ew = reinterpret_cast<const uint32_t*>(&expect);
+            const int l = threadIdx.x;
+            const bool differs = l < kWords && blob[l] != ew[l];
+            const uint64_t any = __ballot(differs);
+            if (l == 0) *status = any ? (uint32_t)MOE_ERR_INVALID : 0u;
+        }
+    }
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -400,14 +418,18 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
 }
 
 hipError_t launch_route(const float* logits, int T, int E, int K, int32_t* ids, float* topw,
-                        uint32_t* misc, hipStream_t s) {
+                        uint32_t* misc, const void* blob, const BlobHeader& expect,
+                        uint32_t* status, hipStream_t s) {
     const dim3 grid((T + 3) / 4), block(256);
     const int epl = (E + 63) / 64;
-    if (epl <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
-    else if (epl <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
-    else if (epl <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
-    else if (epl <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
-    else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, K, ids, topw, misc);
+    const uint32_t* bw = static_cast<const uint32_t*>(blob);
+#define RT(N) hipLaunchKernelGGL(route_topk_kernel<N>, grid, block, 0, s, logits, T, E, K, ids, topw, misc, bw, expect, status)
+    if (epl <= 1) RT(1);
+    else if (epl <= 2) RT(2);
+    else if (epl <= 4) RT(4);
+    else if (epl <= 8) RT(8);
+    else RT(16);
+#undef RT
     return hipGetLastError();
 }
 

@@ -28,7 +28,9 @@
  *    owned by the caller. The library never allocates device or host memory
  *    and keeps no per-call state, except the optional stage timing below.
  *  - Every call only enqueues work on `stream` and returns; no host<->device
- *    synchronisation except in moe_check_prepared and moe_stage_times.
+ *    synchronisation except in moe_check_prepared, moe_forward_status and
+ *    moe_stage_times (and in moe_forward while stage timing is on, see
+ *    moe_stage_timing).
  *  - Argument checks all run before any launch; on failure nothing is
  *    enqueued and a moe_status other than MOE_OK is returned, with a message in
  *    moe_last_error().
@@ -49,7 +51,14 @@ typedef enum {
     MOE_W4A4_TENSOR = 0, /* NVFP4 weights and activations, one activation global scale per tensor */
     MOE_W4A4_TOKEN = 1,  /* NVFP4 weights and activations, one activation global scale per row    */
     MOE_W4A16 = 2,       /* NVFP4 weights, bf16 activations                                         */
-    MOE_MXFP8 = 3        /* MXFP8 (E4M3 + E8M0 per 32) weights and activations                      */
+    MOE_MXFP8 = 3,       /* MXFP8 (E4M3 + E8M0 per 32) weights and activations                      */
+    /* NVFP4 weights; activations per token under the "4-over-6" contract
+     * (FlashInfer PR #4366, "Performance benchmark", named there by its
+     * switches only; this library's reading): global scale amax / (6*256) per
+     * row, and per 16-block the block max mapped to 6 or to 4, whichever gives
+     * the smaller sum of squared errors (fp64, element order; ties to 6). The
+     * GEMMs consume the result like any NVFP4 operand. */
+    MOE_W4A4_TOKEN_4O6 = 4
 } moe_mode;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
@@ -97,7 +106,13 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t 
 
 /* S1..S7: one layer forward.
  *   prepared: blob from moe_prepare_weights with the same `d` (NVFP4 blob for
- *             modes 0..2, MXFP8 blob for mode 3).
+ *             modes 0..2, MXFP8 blob for mode 3), prepared_bytes its size in
+ *             bytes (MOE_ERR_WORKSPACE below moe_prepared_bytes(d)). The blob's
+ *             header is compared with `d` on the device by the forward's first
+ *             kernel: on a difference (a blob prepared for other dimensions,
+ *             activation or format) the forward reads no weights, leaves y
+ *             unwritten and sets its status word to MOE_ERR_INVALID, which
+ *             moe_forward_status returns.
  *   x:        [T][H] bf16 bit patterns.            logits: [T][E] fp32 (finite).
  *   T >= 1, 1 <= K <= min(E, 64), T*K*max(H, I)*2 < 4 GiB (MOE_ERR_UNSUPPORTED
  *   otherwise: the GEMMs address activation rows with 32-bit offsets).
@@ -110,16 +125,25 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t 
  *   order, hence the last bits, may vary run to run).
  *   MXFP8 quantizes the FC2 input in the FC1 epilogue (no fp32 copy).
  *   workspace: >= moe_workspace_bytes(d, T, K, mode) bytes, 256-byte aligned;
- *   afterwards it holds the intermediate views listed by moe_workspace_view.
+ *   afterwards it holds the forward's status word (first 4 bytes) and the
+ *   intermediate views listed by moe_workspace_view.
  *   y: [T][H] bf16 bit patterns (output). */
-int moe_forward(const moe_dims* d, const void* prepared, const uint16_t* x, const float* logits,
-                int32_t T, int32_t K, int32_t mode, int32_t act, int32_t router_weight_on_input,
-                int32_t deterministic_finalize, void* workspace, size_t workspace_bytes,
-                uint16_t* y, hipStream_t stream);
+int moe_forward(const moe_dims* d, const void* prepared, size_t prepared_bytes, const uint16_t* x,
+                const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
+                int32_t router_weight_on_input, int32_t deterministic_finalize, void* workspace,
+                size_t workspace_bytes, uint16_t* y, hipStream_t stream);
+
+/* Status word of the last forward enqueued on `workspace` (synchronous: waits
+ * for `stream`, then reads 4 bytes): *status = 0 after a forward whose blob
+ * header matched its dimensions, MOE_ERR_INVALID otherwise (y was then not
+ * written). Not for use under graph capture. */
+int moe_forward_status(const void* workspace, int32_t* status, hipStream_t stream);
 
 /* S7 alone (unfused finalize, as in PR #5319): y[t][j] = sum_{k<K} w[t][k] *
  * permuted_out[route_to_row[t*K+k]][j], accumulated in fp32 in k order and
- * rounded once to bf16.
+ * rounded once to bf16. Always the fixed-order (deterministic) reduction: the
+ * fused variant exists only inside moe_forward, where it is the FC2
+ * epilogue's scatter-add.
  *   permuted_out: [R][H] fp32 (out_is_bf16 = 0) or bf16 (1), R = T*K.
  *   route_to_row: [T*K] int32, each in [0, R).  weights: [T][K] fp32 or NULL
  *   for unit weights (input-side placement).  y: [T][H] bf16. */
@@ -129,7 +153,8 @@ int moe_finalize(const void* permuted_out, int32_t out_is_bf16, const int32_t* r
 
 /* Standalone block quantizer (the S3/S5 quantizer as a library call).
  *   v: [rows][cols] fp32; kind: 0 = NVFP4 one global scale for the whole
- *   matrix, 1 = NVFP4 one global scale per row, 2 = MXFP8.
+ *   matrix, 1 = NVFP4 one global scale per row, 2 = MXFP8, 3 = NVFP4 per row
+ *   with the 4-over-6 block choice (see MOE_W4A4_TOKEN_4O6).
  *   codes: NVFP4 [rows][cols/2] (two E2M1 codes per byte, even element in the
  *   low nibble); MXFP8 [rows][cols] E4M3.  scales: NVFP4 [rows][cols/16] E4M3;
  *   MXFP8 [rows][cols/32] E8M0.  g: NVFP4 [1] or [rows] fp32 (unused for MXFP8).
@@ -151,7 +176,10 @@ int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32_t mode, in
                        size_t* offset, size_t* bytes);
 
 /* Optional per-stage timing with HIP events recorded on the forward's stream
- * around each stage (not to be enabled under graph capture). moe_stage_times
+ * around each stage (not to be enabled under graph capture). While it is on,
+ * forwards take a process-wide lock for their launches (forwards from several
+ * host threads serialise), and a forward waits for the events of the oldest
+ * of the last 128 timed forwards before reusing them. moe_stage_times
  * synchronises, returns the summed milliseconds per stage since the last
  * reset in ms[0..n) and the number of timed forwards, and resets. Stage ids:
  * 0 route, 1 permute, 2 quantize x, 3 FC1, 4 FC2-input quantize, 5 FC2,

@@ -244,6 +244,67 @@ void orc_nvfp4_quantize(int n, const float* v, float g, uint8_t* codes, uint8_t*
     }
 }
 
+/* ------------------------------------------------------------------------- */
+/* NVFP4 "4-over-6" block choice for per-token activations (FlashInfer PR     */
+/* #4366, "Performance benchmark": the 4-over-6 per-token activation contract, */
+/* named there by its environment switches only). Reading, step by step:      */
+/*  - global scale g = amax / (6 * 256): the block scales of the usual         */
+/*    max-to-6 mapping stay at or below 256, so the max-to-4 mapping (1.5x     */
+/*    larger scales, up to 384) still fits E4M3's 448;                         */
+/*  - per 16-block, two candidates: the usual one (block max mapped to the     */
+/*    E2M1 maximum 6: s = a_b / (6 g)) and the max-to-4 one (s = a_b / (4 g)), */
+/*    each with the same fp32 operation order as orc_nvfp4_quantize;          */
+/*  - the candidate with the smaller sum of squared errors                    */
+/*    sum_i (v_i - code_i * d)^2 over the block is kept, ties going to the     */
+/*    usual one. The error is accumulated in fp64 in element order, each       */
+/*    operation rounded once, so the decision is reproducible.                 */
+/* ------------------------------------------------------------------------- */
+
+float orc_nvfp4_global_scale_4o6(float amax) { return amax / 1536.0f; }
+
+/* One 16-block with global scale g and the block max mapped to `top` (6 or
+ * 4): writes the codes, returns the E4M3 scale code and the block's sum of
+ * squared errors (fp64, element order). */
+static int nvfp4_block_candidate(const float* vb, float g, float top, uint8_t* cb, double* err) {
+    float ab = orc_absmax(vb, 16);
+    float top_g = top * g;
+    float s = ab / top_g;
+    int sfc = orc_e4m3_encode((double)s);
+    float d = (float)orc_e4m3_decode(sfc) * g;
+    double e = 0.0;
+    for (int i = 0; i < 16; ++i) {
+        if (d == 0.0f) {
+            cb[i] = signbit(vb[i]) ? 8 : 0;
+        } else {
+            float u = vb[i] / d;
+            cb[i] = (uint8_t)orc_e2m1_encode((double)u);
+        }
+        double diff = (double)vb[i] - orc_e2m1_decode(cb[i]) * (double)d;
+        e = e + diff * diff;
+    }
+    *err = e;
+    return sfc;
+}
+
+void orc_nvfp4_quantize_4o6(int n, const float* v, float g, uint8_t* codes, uint8_t* sf) {
+    for (int b = 0; b < n / 16; ++b) {
+        const float* vb = v + (size_t)b * 16;
+        uint8_t* cb = codes + (size_t)b * 16;
+        if (g == 0.0f) {
+            sf[b] = 0;
+            for (int i = 0; i < 16; ++i) cb[i] = signbit(vb[i]) ? 8 : 0;
+            continue;
+        }
+        uint8_t c6[16], c4[16];
+        double e6, e4;
+        int s6 = nvfp4_block_candidate(vb, g, 6.0f, c6, &e6);
+        int s4 = nvfp4_block_candidate(vb, g, 4.0f, c4, &e4);
+        int four = e4 < e6;
+        sf[b] = (uint8_t)(four ? s4 : s6);
+        memcpy(cb, four ? c4 : c6, 16);
+    }
+}
+
 /* Dequantized value code * sf * g, exact in fp64 (at most 2 + 4 + 24 bits). */
 void orc_nvfp4_dequant(int n, const uint8_t* codes, const uint8_t* sf, float g, double* out) {
     for (int i = 0; i < n; ++i)

@@ -28,6 +28,8 @@ void orc_permute(int T, int K, int E, const int32_t* ids, int32_t* counts, int32
 float orc_absmax(const float* v, size_t n);
 float orc_nvfp4_global_scale(float amax);
 void orc_nvfp4_quantize(int n, const float* v, float g, uint8_t* codes, uint8_t* sf);
+float orc_nvfp4_global_scale_4o6(float amax);
+void orc_nvfp4_quantize_4o6(int n, const float* v, float g, uint8_t* codes, uint8_t* sf);
 void orc_nvfp4_dequant(int n, const uint8_t* codes, const uint8_t* sf, float g, double* out);
 void orc_mxfp8_quantize(int n, const float* v, uint8_t* codes, uint8_t* sc);
 void orc_mxfp8_dequant(int n, const uint8_t* codes, const uint8_t* sc, double* out);

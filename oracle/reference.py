@@ -35,7 +35,9 @@ _SRC = os.path.join(_HERE, "moe_oracle.c")
 
 FMT_NVFP4, FMT_MXFP8 = 0, 1
 ACT_SWIGLU, ACT_RELU2 = 0, 1
-MODES = ("w4a4_tensor", "w4a4_token", "w4a16", "mxfp8")
+MODES = ("w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6")
+# modes whose activations carry one NVFP4 global scale per row (token / route)
+PER_ROW_MODES = ("w4a4_token", "w4a4_token_4o6")
 
 
 def build(force: bool = False) -> str:
@@ -68,6 +70,8 @@ def lib():
         L.orc_absmax.restype = f; L.orc_absmax.argtypes = [P, ctypes.c_size_t]
         L.orc_nvfp4_global_scale.restype = f; L.orc_nvfp4_global_scale.argtypes = [f]
         L.orc_nvfp4_quantize.restype = None; L.orc_nvfp4_quantize.argtypes = [i, P, f, P, P]
+        L.orc_nvfp4_global_scale_4o6.restype = f; L.orc_nvfp4_global_scale_4o6.argtypes = [f]
+        L.orc_nvfp4_quantize_4o6.restype = None; L.orc_nvfp4_quantize_4o6.argtypes = [i, P, f, P, P]
         L.orc_nvfp4_dequant.restype = None; L.orc_nvfp4_dequant.argtypes = [i, P, P, f, P]
         L.orc_mxfp8_quantize.restype = None; L.orc_mxfp8_quantize.argtypes = [i, P, P, P]
         L.orc_mxfp8_dequant.restype = None; L.orc_mxfp8_dequant.argtypes = [i, P, P, P]
@@ -151,23 +155,28 @@ def absmax(v: np.ndarray) -> np.float32:
     return np.float32(lib().orc_absmax(_p(v), v.size))
 
 
-def nvfp4_quantize(v: np.ndarray, per_row: bool, threads: int = 1):
+def nvfp4_quantize(v: np.ndarray, per_row: bool, threads: int = 1, four_over_six: bool = False):
     """NVFP4 of a [rows, n] fp32 matrix; one global scale for the whole matrix
-    (per_row=False) or one per row. Returns unpacked codes [rows, n] u8, block
-    scales [rows, n/16] u8 (E4M3 bits) and g ([1] or [rows]) fp32."""
+    (per_row=False) or one per row. four_over_six: the 4-over-6 block choice
+    (orc_nvfp4_quantize_4o6, one global scale per row only). Returns unpacked
+    codes [rows, n] u8, block scales [rows, n/16] u8 (E4M3 bits) and g ([1] or
+    [rows]) fp32."""
     v = np.ascontiguousarray(v, dtype=np.float32)
     rows, n = v.shape
     L = lib()
     codes = np.empty((rows, n), np.uint8)
     sf = np.empty((rows, n // 16), np.uint8)
+    assert per_row or not four_over_six, "4-over-6 is a per-token contract"
+    gscale = L.orc_nvfp4_global_scale_4o6 if four_over_six else L.orc_nvfp4_global_scale
+    quant = L.orc_nvfp4_quantize_4o6 if four_over_six else L.orc_nvfp4_quantize
     if per_row:
-        g = np.array([L.orc_nvfp4_global_scale(absmax(v[r])) for r in range(rows)], np.float32)
+        g = np.array([gscale(absmax(v[r])) for r in range(rows)], np.float32)
     else:
-        g = np.array([L.orc_nvfp4_global_scale(absmax(v))], np.float32)
+        g = np.array([gscale(absmax(v))], np.float32)
 
     def one(r):
         gr = float(g[r] if per_row else g[0])
-        L.orc_nvfp4_quantize(n, _p(v[r]), gr, _p(codes[r]), _p(sf[r]))
+        quant(n, _p(v[r]), gr, _p(codes[r]), _p(sf[r]))
     _pmap(one, range(rows), threads)
     return codes, sf, g
 
@@ -256,15 +265,28 @@ class QuantWeights:
         lib().orc_expert_matvec(self.fmt, self.H, self.I, _p(c), _p(s), float(g), _p(a), _p(out))
         return out
 
+    def dequant_matrix(self, e, which: int) -> np.ndarray:
+        """Dense fp64 dequantized W1 [N1, H] (which = 0) or W2 [H, I] (which = 1)
+        of expert e, each element decoded by the oracle's own codec (exact)."""
+        c, s, g = self.q[e][which]
+        N = c.shape[0]
+        if self.fmt == FMT_NVFP4:
+            return nvfp4_dequant(c, s, np.array([g] * N, np.float32), per_row=True)
+        return mxfp8_dequant(c, s)
+
     def dequant(self, e):
         """Dense fp64 dequantized (W1 [N1, H], W2 [H, I]) of expert e."""
-        out = []
-        for (c, s, g), (N, K) in zip(self.q[e], [(self.N1, self.H), (self.H, self.I)]):
-            if self.fmt == FMT_NVFP4:
-                out.append(nvfp4_dequant(c, s, np.array([g] * N, np.float32), per_row=True))
-            else:
-                out.append(mxfp8_dequant(c, s))
-        return out
+        return [self.dequant_matrix(e, 0), self.dequant_matrix(e, 1)]
+
+    def fc1_rows(self, e, A: np.ndarray) -> np.ndarray:
+        """FC1 of several fp64 input rows A [n, H] for expert e: one fp64 matrix
+        product with the dequantized W1 (the grouped GEMM by its definition; the
+        library matmul only changes the fp64 summation order)."""
+        return np.ascontiguousarray(A, dtype=np.float64) @ self.dequant_matrix(e, 0).T
+
+    def fc2_rows(self, e, A: np.ndarray) -> np.ndarray:
+        """FC2 of several fp64 input rows A [n, I] for expert e (as fc1_rows)."""
+        return np.ascontiguousarray(A, dtype=np.float64) @ self.dequant_matrix(e, 1).T
 
 
 # --------------------------------------------------------------------------
@@ -281,8 +303,8 @@ def quantize_x(x_bits: np.ndarray, mode: str, threads: int = 1) -> dict:
         codes, sc = mxfp8_quantize(x, threads)
         return {"codes": codes, "scales": sc,
                 "deq": lambda t: mxfp8_dequant(codes[t:t + 1], sc[t:t + 1])[0]}
-    per_row = mode == "w4a4_token"
-    codes, sf, g = nvfp4_quantize(x, per_row, threads)
+    per_row = mode in PER_ROW_MODES
+    codes, sf, g = nvfp4_quantize(x, per_row, threads, four_over_six=mode == "w4a4_token_4o6")
     return {"codes": codes, "scales": sf, "g": g,
             "deq": lambda t: nvfp4_dequant(codes[t:t + 1], sf[t:t + 1],
                                            g[t:t + 1] if per_row else g, per_row)[0]}
@@ -292,14 +314,79 @@ def quantize_x(x_bits: np.ndarray, mode: str, threads: int = 1) -> dict:
 # the layer
 # --------------------------------------------------------------------------
 
+def _blas_single_thread():
+    """Context that keeps BLAS to one thread inside the oracle's own thread pool
+    (each worker runs its own matrix product)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(limits=1, user_api="blas")
+    except ImportError:  # pragma: no cover
+        import contextlib
+        return contextlib.nullcontext()
+
+
+def _by_expert(routes, ids):
+    """{expert: [routes in ascending order]} for the given routes."""
+    groups = {}
+    for r in routes:
+        groups.setdefault(int(ids.flat[r]), []).append(int(r))
+    return groups
+
+
+def fc2_finalize(W: QuantWeights, ids: np.ndarray, p: np.ndarray, K: int, on_input: bool,
+                 tokens, a2_of_route, threads: int = 1, batched: bool = False):
+    """S6 + S7 for the given tokens: o_r = W2_{e(r)} a2_r for every route r of
+    those tokens (fp64), then y[t] = sum_{k<K} w_{t,k} o_{tK+k} in fixed k order
+    (fp64), w = p for output-side placement and 1 for input-side placement
+    (neutral finalize weights, FlashInfer PR #4366, "Description").
+
+    a2_of_route(r) gives route r's fp64 FC2 input row (the dequantized FC2
+    input). Returns (o [len(tokens)*K, H] in route order, y [len(tokens), H])."""
+    toks = [int(t) for t in tokens]
+    want = [t * K + k for t in toks for k in range(K)]
+    H = W.H
+    if not want:
+        return np.zeros((0, H)), np.zeros((0, H))
+    if batched:
+        groups = _by_expert(want, ids)
+
+        def one(item):
+            e, rs = item
+            return rs, W.fc2_rows(e, np.stack([a2_of_route(r) for r in rs]))
+        pos = {r: i for i, r in enumerate(want)}
+        o = np.empty((len(want), H), np.float64)
+        with _blas_single_thread() if threads > 1 else _nullctx():
+            for rs, block in _pmap(one, sorted(groups.items()), threads):
+                o[[pos[r] for r in rs]] = block
+    else:
+        o = np.stack(_pmap(lambda r: W.fc2(int(ids.flat[r]), np.ascontiguousarray(a2_of_route(r))),
+                           want, threads))
+    # S7: finalize in fixed k order; unit weights for input-side placement
+    w = None if on_input else np.ascontiguousarray(p[toks], dtype=np.float64)
+    y = np.empty((len(toks), H), np.float64)
+    lib().orc_finalize(len(toks), K, H, _p(np.ascontiguousarray(o)),
+                       _p(np.arange(len(want), dtype=np.int32)),
+                       _p(w) if w is not None else None, _p(y))
+    return o, y
+
+
+def _nullctx():
+    import contextlib
+    return contextlib.nullcontext()
+
+
 def forward(x_bits: np.ndarray, logits: np.ndarray, W: QuantWeights, K: int, mode: str,
             act: str, on_input: bool, tokens=None, threads: int = 1,
-            fc2_input_quant: bool = True, pre_act_variant: bool = False) -> dict:
+            fc2_input_quant: bool = True, pre_act_variant: bool = False,
+            batched: bool = False) -> dict:
     """One MoE layer forward in fp64 (except the fp32 quantizer arithmetic).
 
     tokens: None for every token, or a list of token ids whose outputs are
     wanted (FC1 still runs over every route when the FC2 input has one
     per-tensor scale, because that scale is the amax over all routes).
+    batched: FC1 and FC2 as one fp64 matrix product per expert over its routes
+    (fc1_rows / fc2_rows) instead of one matrix-vector product per route; the
+    results differ only in the fp64 summation order.
     fc2_input_quant=False and pre_act_variant=True are test-only switches
     (linearity check of the placement; the deliberately wrong pre-activation
     scaling) and are never used for parity.
@@ -323,14 +410,32 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, W: QuantWeights, K: int, mod
     fc1_routes = list(range(T * K)) if per_tensor_fc2 else want
     W.ensure({int(ids.flat[r]) for r in fc1_routes}, threads)
 
-    def fc1(r):                                                      # S4 + S5 (act, placement)
-        t, e = r // K, int(ids.flat[r])
-        h = W.fc1(e, xq["deq"](t))
+    def activate(r, h):                                              # S5 (act, placement)
         a = np.empty(I, np.float64)
-        lib().orc_activation(ACT_SWIGLU if act == "swiglu" else ACT_RELU2, I, _p(h),
-                             int(on_input), float(p.flat[r]), int(pre_act_variant), _p(a))
+        lib().orc_activation(ACT_SWIGLU if act == "swiglu" else ACT_RELU2, I,
+                             _p(np.ascontiguousarray(h)), int(on_input), float(p.flat[r]),
+                             int(pre_act_variant), _p(a))
         return a
-    a = np.stack(_pmap(fc1, fc1_routes, threads)) if fc1_routes else np.zeros((0, I))
+
+    if not fc1_routes:
+        a = np.zeros((0, I))
+    elif batched:                                                    # S4, per expert
+        groups = _by_expert(fc1_routes, ids)
+
+        def one(item):
+            e, rs = item
+            h = W.fc1_rows(e, np.stack([xq["deq"](r // K) for r in rs]))
+            return rs, [activate(r, h[i]) for i, r in enumerate(rs)]
+        pos = {r: i for i, r in enumerate(fc1_routes)}
+        a = np.empty((len(fc1_routes), I), np.float64)
+        with _blas_single_thread() if threads > 1 else _nullctx():
+            for rs, rows in _pmap(one, sorted(groups.items()), threads):
+                for r, row in zip(rs, rows):
+                    a[pos[r]] = row
+    else:
+        def fc1(r):                                                  # S4, per route
+            return activate(r, W.fc1(int(ids.flat[r]), xq["deq"](r // K)))
+        a = np.stack(_pmap(fc1, fc1_routes, threads))
     a_idx = {r: i for i, r in enumerate(fc1_routes)}
     out["a_routes"] = np.array(fc1_routes, np.int64)
     out["a"] = a
@@ -346,26 +451,13 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, W: QuantWeights, K: int, mod
         out["a2q"] = {"codes": c2, "scales": s2}
         a2 = mxfp8_dequant(c2, s2)
     else:
-        per_row = mode == "w4a4_token"
-        c2, s2, g2 = nvfp4_quantize(a32, per_row, threads)
+        per_row = mode in PER_ROW_MODES
+        c2, s2, g2 = nvfp4_quantize(a32, per_row, threads, four_over_six=mode == "w4a4_token_4o6")
         out["a2q"] = {"codes": c2, "scales": s2, "g": g2}
         a2 = nvfp4_dequant(c2, s2, g2, per_row)
 
-    def fc2(r):                                                      # S6
-        return W.fc2(int(ids.flat[r]), np.ascontiguousarray(a2[a_idx[r]]))
-    o = np.stack(_pmap(fc2, want, threads)) if want else np.zeros((0, H))
-
-    # S7: finalize in fixed k order; unit weights for input-side placement
-    if tokens is None:
-        o_perm = np.empty((T * K, H), np.float64)
-        o_perm[rt2row] = o                 # row rt2row[r] holds route r's output
-        o_src, map_ = o_perm, rt2row
-    else:
-        o_src, map_ = np.ascontiguousarray(o), np.arange(len(want), dtype=np.int32)
-    w = None if on_input else np.ascontiguousarray(p[toks])
-    y = np.empty((len(toks), H), np.float64)
-    lib().orc_finalize(len(toks), K, H, _p(o_src), _p(np.ascontiguousarray(map_, np.int32)),
-                       _p(w) if w is not None else None, _p(y))
+    # S6 + S7
+    o, y = fc2_finalize(W, ids, p, K, on_input, toks, lambda r: a2[a_idx[r]], threads, batched)
     out["o"] = o
     out["tokens"] = np.array(toks, np.int64)
     out["y"] = y

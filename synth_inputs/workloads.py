@@ -17,7 +17,7 @@ class Workload:
     I: int
     E: int
     K: int
-    mode: str          # "w4a4_tensor" | "w4a4_token" | "w4a16" | "mxfp8"
+    mode: str          # "w4a4_tensor" | "w4a4_token" | "w4a16" | "mxfp8" | "w4a4_token_4o6"
     act: str           # "swiglu" | "relu2"
     on_input: bool     # router weight applied before FC2 (input side)
     finalize: tuple    # finalize variants exercised: ("det",), ("fused",), ("det", "fused")
@@ -46,6 +46,9 @@ WORKLOADS = {
                  "w4a16", "swiglu", False, ("det", "fused"), "uniform"),
         Workload("prefill_w4a4_token_T4096_H4096_I2048_E128_K8", 4096, 4096, 2048, 128, 8,
                  "w4a4_token", "swiglu", True, ("det", "fused"), "normal_bias"),
+        # the same prefill layer under the 4-over-6 per-token activation contract
+        Workload("prefill_w4a4_token4o6_T4096_H4096_I2048_E128_K8", 4096, 4096, 2048, 128, 8,
+                 "w4a4_token_4o6", "swiglu", True, ("det", "fused"), "normal_bias"),
         Workload("decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8", 64, 7168, 2048, 256, 8,
                  "w4a4_tensor", "relu2", True, ("det",), "uniform"),
         Workload("prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8", 16384, 7168, 2048, 256, 8,

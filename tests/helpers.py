@@ -16,11 +16,12 @@ from synth_inputs.gen import STREAM_W1, STREAM_W2, make_weight
 MAX_ERR_RMS = 2e-2
 REL_FRO = 1e-2
 TOPW_REL = 1e-6
-# The output is bf16 by the interface: rounding even the exact result costs up
-# to BF16_U * |y| per element (unit roundoff 2^-8). On heavy-tailed outputs
-# that alone can exceed 2e-2 * rms (measured up to 2.5e-2 on shapes outside
+# The output is bf16 by the interface: rounding the GPU's fp32 result y32 to
+# bf16 (8 significant bits, round to nearest even) moves it by at most half a
+# bf16 ulp of y32, and that half ulp is at most half an ulp of the rounded
+# value y_gpu (RNE never lands in a lower binade). On heavy-tailed outputs that
+# rounding alone can exceed 2e-2 * rms (measured up to 2.5e-2 on shapes outside
 # the named workloads), so tests of arbitrary shapes bound the error beyond it.
-BF16_U = 2.0 ** -8
 
 
 def bits16(t: torch.Tensor) -> np.ndarray:
@@ -31,13 +32,19 @@ def bf16_to_f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().float().numpy().astype(np.float64)
 
 
+def half_ulp_bf16(y: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at each value: 2^(floor(log2|y|) - 8) (0 for y = 0)."""
+    m, ex = np.frexp(np.abs(y))            # |y| = m 2^ex, m in [0.5, 1)
+    return np.where(y != 0, np.ldexp(1.0, ex - 9), 0.0)
+
+
 def out_errors(y_gpu: np.ndarray, y_ref: np.ndarray, round_allow=False):
     """max|err|/rms and the relative Frobenius error; with round_allow the max
-    is taken over |err| - BF16_U * |y_ref| (the error beyond the output's own
-    bf16 rounding)."""
+    is taken over |err| - half_ulp_bf16(y_gpu) (the error beyond the output's
+    own bf16 rounding)."""
     err = y_gpu - y_ref
     rms = math.sqrt(float(np.mean(y_ref * y_ref)))
-    e = np.abs(err) - BF16_U * np.abs(y_ref) if round_allow else np.abs(err)
+    e = np.abs(err) - half_ulp_bf16(y_gpu) if round_allow else np.abs(err)
     max_rel = float(np.max(e)) / rms
     fro = float(np.linalg.norm(err) / np.linalg.norm(y_ref))
     return max_rel, fro
@@ -200,21 +207,24 @@ def unpack_nibbles(packed: np.ndarray, n: int) -> np.ndarray:
 # (measured <= 2.5e-7 at H=256); the block-scaled fp8 matrix core rounds
 # inside each 128-deep instruction more coarsely (measured up to 7.4e-5), so
 # its bound is wider. Both bounds carry a margin over the measurements.
-TAU = {"w4a4_tensor": 2.0 ** -18, "w4a4_token": 2.0 ** -18, "w4a16": 2.0 ** -18,
+TAU = {"w4a4_tensor": 2.0 ** -18, "w4a4_token": 2.0 ** -18, "w4a4_token_4o6": 2.0 ** -18,
+       "w4a16": 2.0 ** -18,
        "mxfp8": 2.0 ** -11}
 
 
 def check_prequant(a_gpu_perm: np.ndarray, ref: dict, mode: str, what=""):
     """a_gpu_perm: the GPU's FC2 input before quantization, [R][I] in permuted
-    row order (fp32, or bf16 values for W4A16). Compares the oracle's routes."""
+    row order (fp32, or bf16 values for W4A16). Compares the oracle's routes:
+    |a_gpu - a_ref| <= TAU * rowmax (+ half a bf16 ulp of the stored value for
+    W4A16, whose FC2 input is that rounding of the fp32 activation)."""
     routes = ref["a_routes"]
     rows = ref["route_to_row"][routes]
     a_ref = ref["a"]
     a_g = a_gpu_perm[rows].astype(np.float64)
     scale = np.abs(a_ref).max(1, keepdims=True) + 1e-300
     bound = TAU[mode] * scale
-    if mode == "w4a16":  # the GPU stores bf16: one bf16 rounding on top
-        bound = bound + 2.0 ** -8 * np.abs(a_ref)
+    if mode == "w4a16":
+        bound = bound + half_ulp_bf16(a_g)
     excess = np.abs(a_g - a_ref) - bound
     assert np.all(excess <= 0), \
         f"{what}: FC1+activation differs from the oracle beyond the bound " \
@@ -262,85 +272,207 @@ def check_a2_mxfp8(codes_perm: np.ndarray, scales_perm: np.ndarray, ref: dict, w
         f"{what}: {int(bad.sum())} MXFP8 FC2-input elements off the oracle's rounding cell"
 
 
-def check_fc2_input(moe, d, ws, T: int, K: int, mode: str, ref: dict, what=""):
-    """The FC2 input the GPU produced, against the oracle's FC1 + activation."""
-    I = d.I
-    if mode == "mxfp8":
-        codes = moe.workspace_view(d, ws, T, K, mode, "a2_codes").cpu().numpy().reshape(T * K, I)
-        scales = moe.workspace_view(d, ws, T, K, mode, "a2_scales").cpu().numpy().reshape(T * K, I // 32)
-        return check_a2_mxfp8(codes, scales, ref, what)
-    a_pre = moe.workspace_view(d, ws, T, K, mode, "a2_pre").float().cpu().numpy()
-    return check_prequant(a_pre.reshape(T * K, I), ref, mode, what)
 
 
-def _requant_row(a32: np.ndarray, mode: str, g_tensor):
-    """Dequantized FC2 input of one route row, as the oracle quantizes it."""
-    from oracle import reference as Rr
-    row = a32[None, :]
-    if mode == "mxfp8":
-        return Rr.mxfp8_dequant(*Rr.mxfp8_quantize(row))[0]
+# ---------------------------------------------------------------------------
+# the FC2 input the GPU produced (S5) and the layer output
+# ---------------------------------------------------------------------------
+# E2M1 rounding cells: code magnitude m is the round-to-nearest-even result
+# for |u| in [CELL_LO[m], CELL_HI[m]] (ties belong to the even neighbour; the
+# checks below accept either side of a tie anyway).
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+CELL_LO = np.array([0.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+CELL_HI = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, np.inf])
+_E4M3_TABLE = None
+
+
+def _e4m3_table():
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = np.array([R.e4m3_decode(c) if (c & 0x7F) != 0x7F else np.nan
+                                for c in range(256)])
+    return _E4M3_TABLE
+
+
+def _fl32(x):
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+class Fc2Input:
+    """The FC2 input of one forward as the GPU left it in the workspace, rows in
+    permuted order: `pre` is the value before quantization (fp32 for W4A4,
+    the stored bf16 values for W4A16, None for MXFP8, which quantizes in the
+    FC1 epilogue), `codes` unpacked one per byte, `scales`, and `g` ([1] per
+    tensor or [R] per route, NVFP4 only)."""
+
+    def __init__(self, mode, pre=None, codes=None, scales=None, g=None):
+        self.mode, self.pre, self.codes, self.scales, self.g = mode, pre, codes, scales, g
+
+    def dequant_row(self, row: int) -> np.ndarray:
+        """The fp64 FC2 input row the GPU's FC2 consumed (its own codes)."""
+        m = self.mode
+        if m == "w4a16":
+            return self.pre[row].astype(np.float64)
+        if m == "mxfp8":
+            return R.mxfp8_dequant(self.codes[row:row + 1], self.scales[row:row + 1])[0]
+        per_row = m in R.PER_ROW_MODES
+        g = self.g[row:row + 1] if per_row else self.g[:1]
+        return R.nvfp4_dequant(self.codes[row:row + 1], self.scales[row:row + 1], g,
+                               per_row=per_row)[0]
+
+
+def read_fc2_input(moe, d, ws, T: int, K: int, mode: str) -> Fc2Input:
+    R_, I = T * K, d.I
+
+    def v(name):
+        return moe.workspace_view(d, ws, T, K, mode, name).cpu().numpy()
     if mode == "w4a16":
-        return Rr.bf16_bits_to_f32(Rr.f32_to_bf16_bits(row)).astype(np.float64)
-    if mode == "w4a4_token":
-        c, s, g = Rr.nvfp4_quantize(row, per_row=True)
-        return Rr.nvfp4_dequant(c, s, g, per_row=True)[0]
-    n = a32.size
-    codes = np.empty(n, np.uint8)
-    sf = np.empty(n // 16, np.uint8)
-    L = Rr.lib()
-    L.orc_nvfp4_quantize(n, Rr._p(np.ascontiguousarray(a32)), float(g_tensor), Rr._p(codes),
-                         Rr._p(sf))
-    return Rr.nvfp4_dequant(codes[None], sf[None], np.array([g_tensor], np.float32), False)[0]
+        return Fc2Input(mode, pre=moe.workspace_view(d, ws, T, K, mode, "a2_pre").float()
+                        .cpu().numpy().reshape(R_, I))
+    if mode == "mxfp8":
+        return Fc2Input(mode, codes=v("a2_codes").reshape(R_, I),
+                        scales=v("a2_scales").reshape(R_, I // 32))
+    return Fc2Input(mode, pre=v("a2_pre").reshape(R_, I),
+                    codes=unpack_nibbles(v("a2_codes"), I).reshape(R_, I),
+                    scales=v("a2_scales").reshape(R_, I // 16),
+                    g=v("a2_g")[:R_ if mode in R.PER_ROW_MODES else 1])
 
 
-def assert_output_close_flips(y_gpu: np.ndarray, ref: dict, W, mode: str, K: int,
-                              on_input: bool, what="", round_allow=False):
-    """The output bar, allowing FC2-input rounding decisions that are ambiguous.
+def check_s5_quantizer(gi: Fc2Input, threads: int = 1, what=""):
+    """NVFP4 FC2-input quantization, bit-exact: the GPU's codes, block scales
+    and global scale(s) of every route equal the oracle's quantizer applied to
+    the GPU's own fp32 values before quantization (per-tensor g from the amax
+    of all R*I values, or one g per route)."""
+    per_row = gi.mode in R.PER_ROW_MODES
+    codes, sf, g = R.nvfp4_quantize(gi.pre, per_row, threads,
+                                    four_over_six=gi.mode == "w4a4_token_4o6")
+    assert np.array_equal(gi.g, g), f"{what}: FC2-input global scale(s) differ from the oracle's quantizer"
+    assert np.array_equal(gi.scales, sf), \
+        f"{what}: {int((gi.scales != sf).sum())} FC2-input block scales differ from the oracle's quantizer"
+    assert np.array_equal(gi.codes, codes), \
+        f"{what}: {int((gi.codes != codes).sum())} FC2-input codes differ from the oracle's quantizer"
 
-    Where the oracle's pre-quantization value of an FC2-input element lies
-    within TAU[mode] * rowmax of a rounding boundary (of the element or of its
-    block or row scale), either side of the boundary is a correct result of
-    the method. For tokens over the bar, the oracle lists those alternatives
-    (from its own values only) and the expected output is moved to the
-    alternative the GPU output is closest to; then the usual bar applies."""
-    y_ref = ref["y"]
-    try:
-        return assert_output_close(y_gpu, y_ref, what, round_allow)
-    except AssertionError:
-        pass
-    rms = math.sqrt(float(np.mean(y_ref * y_ref)))
-    y_exp = y_ref.copy()
-    pos = {int(r): i for i, r in enumerate(ref["a_routes"])}
-    g_t = ref.get("a2q", {}).get("g", [0.0])[0]
-    toks = ref["tokens"]
-    excess = np.abs(y_gpu - y_exp) - (BF16_U * np.abs(y_exp) if round_allow else 0.0)
-    bad = np.where(excess.max(1) > MAX_ERR_RMS * rms)[0]
-    taken = considered = 0
-    for row in bad:
-        t = int(toks[row])
-        for k in range(K):
-            r = t * K + k
-            e = int(ref["ids"][t, k])
-            wk = 1.0 if on_input else float(ref["p"][t, k])
-            a32 = ref["a"][pos[r]].astype(np.float32)
-            deq0 = _requant_row(a32, mode, g_t)
-            eps = np.float32(TAU[mode] * float(np.abs(a32).max()))
-            w2 = W.dequant(e)[1]
-            alts = []
-            for i in range(a32.size):
-                for sgn in (1.0, -1.0):
-                    a2 = a32.copy()
-                    a2[i] = np.float32(a32[i] + np.float32(sgn) * eps)
-                    d = _requant_row(a2, mode, g_t) - deq0
-                    if np.any(d != 0):
-                        alts.append(d)
-            considered += len(alts)
-            for d in sorted(alts, key=lambda v: -float(np.abs(v).sum())):
-                eff = wk * (w2 @ d)
-                res = y_gpu[row] - y_exp[row]
-                if float(res @ eff) > 0.5 * float(eff @ eff):
-                    y_exp[row] += eff
-                    taken += 1
-    return assert_output_close(
-        y_gpu, y_exp, f"{what} ({taken} of {considered} ambiguous FC2-input roundings re-taken)",
-        round_allow)
+
+def check_a2_nvfp4(gi: Fc2Input, ref: dict, what=""):
+    """NVFP4 FC2 input against the oracle's fp64 activation v of each sampled
+    route (twin of check_a2_mxfp8), with eps = TAU * rowmax the FC1
+    accumulation-order allowance (the GPU's fp32 values may differ from v by
+    up to eps):
+      - the global scale is fl32(fl32(A)/2688) for an amax A within eps of
+        the oracle's (over all routes per tensor, over the row per route);
+      - each block scale is the E4M3 rounding of fl32(a_b / fl32(6 g)) for a
+        block max a_b within eps of the oracle's, g being the GPU's own (for
+        the 4-over-6 contract: global scale fl32(A)/1536, and the block
+        scale either that or the max-to-4 one, fl32(a_b / fl32(4 g)));
+      - each code's E2M1 rounding cell, at the decode scale d = fl32(sf g) of
+        the GPU's own scales, lies within eps / d of v / d, with v's sign
+        wherever |v| > eps; a zero decode scale leaves sign-only codes."""
+    mode = gi.mode
+    routes = ref["a_routes"]
+    rows = ref["route_to_row"][routes]
+    v = ref["a"]
+    n, I = v.shape
+    tau = TAU[mode]
+    rowmax = np.abs(v).max(1)
+    eps = tau * rowmax
+    tab = _e4m3_table()
+    # global scale
+    f46 = mode == "w4a4_token_4o6"
+    gdiv = 1536.0 if f46 else 2688.0
+    if mode in R.PER_ROW_MODES:
+        g = gi.g[rows].astype(np.float64)
+        glo = _fl32(_fl32(np.maximum(rowmax - eps, 0.0)) / gdiv)
+        ghi = _fl32(_fl32(rowmax + eps) / gdiv)
+    else:
+        assert len(routes) == ref["route_to_row"].size, "per-tensor scale needs every route"
+        A = float(rowmax.max())
+        g = np.full(n, float(gi.g[0]))
+        glo = np.full(n, float(_fl32(_fl32(max(A - tau * A, 0.0)) / 2688.0)))
+        ghi = np.full(n, float(_fl32(_fl32(A + tau * A) / 2688.0)))
+    bad_g = (g < glo) | (g > ghi)
+    assert not bad_g.any(), f"{what}: {int(bad_g.sum())} FC2-input global scales outside the allowed range"
+    # block scales
+    ab = np.abs(v).reshape(n, I // 16, 16).max(2)
+    sf = gi.scales[rows].astype(np.int64)
+    enc = np.vectorize(lambda x: R.e4m3_encode(float(x)), otypes=[np.int64])
+
+    def scale_range(top):
+        top_g = _fl32(top * g)[:, None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            s_lo = np.where(top_g > 0, _fl32(_fl32(np.maximum(ab - eps[:, None], 0.0)) / top_g), 0.0)
+            s_hi = np.where(top_g > 0, _fl32(_fl32(ab + eps[:, None]) / top_g), 0.0)
+        return enc(s_lo), enc(s_hi), top_g
+    lo, hi, six_g = scale_range(6.0)
+    ok_s = (sf >= lo) & (sf <= hi)
+    if f46:
+        lo4, hi4, _ = scale_range(4.0)
+        ok_s |= (sf >= lo4) & (sf <= hi4)
+    bad_s = ~ok_s | ((six_g == 0) & (sf != 0))
+    assert not bad_s.any(), f"{what}: {int(bad_s.sum())} FC2-input block scales outside the allowed range"
+    # element codes
+    c = gi.codes[rows].astype(np.int64)
+    m, neg = c & 7, (c & 8) != 0
+    d = _fl32(tab[sf] * g[:, None])                     # [n, I/16]
+    d = np.repeat(d, 16, axis=1)
+    e = np.repeat(eps[:, None], I, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(d > 0, np.abs(v) / d, 0.0)
+        du = np.where(d > 0, e / d, 0.0)
+    in_cell = (u >= CELL_LO[m] - du) & (u <= CELL_HI[m] + du)
+    ok = np.where(d > 0, in_cell, m == 0)
+    sign_ok = (neg == np.signbit(v)) | (np.abs(v) <= e)
+    bad = ~(ok & sign_ok)
+    assert not bad.any(), \
+        f"{what}: {int(bad.sum())} NVFP4 FC2-input codes off the oracle's rounding cell " \
+        f"(first at sampled route {int(np.argwhere(bad)[0][0])})"
+
+
+def check_fc2_input(gi: Fc2Input, ref: dict, threads: int = 1, what=""):
+    """Every check of the FC2 input the GPU produced (S5)."""
+    if gi.mode == "mxfp8":
+        return check_a2_mxfp8(gi.codes, gi.scales, ref, what)
+    check_prequant(gi.pre, ref, gi.mode, what)
+    if gi.mode != "w4a16":
+        check_s5_quantizer(gi, threads, what)
+        check_a2_nvfp4(gi, ref, what)
+
+
+def expected_from_own_fc2_input(gi: Fc2Input, ref: dict, W, K: int, on_input: bool,
+                                threads: int = 1) -> np.ndarray:
+    """The oracle's FC2 and finalize (fp64) run on the FC2 input the GPU itself
+    produced, for the oracle's tokens: the layer output the GPU must reproduce
+    given its own FC2-input rounding decisions, which check_fc2_input has
+    already tied to the oracle's FC1 and activation."""
+    r2row = ref["route_to_row"]
+    _, y = R.fc2_finalize(W, ref["ids"], ref["p"], K, on_input, ref["tokens"],
+                          lambda r: gi.dequant_row(int(r2row[r])), threads, batched=True)
+    return y
+
+
+def check_layer_output(y_gpu: np.ndarray, gi: Fc2Input, ref: dict, W, K: int, on_input: bool,
+                       what="", round_allow=False, threads: int = 1):
+    """The layer output y_gpu (bf16 values, rows of ref["tokens"]) at the plain
+    bar (max|err| <= 2e-2 rms, relative Frobenius <= 1e-2; with round_allow
+    the max counts the error beyond the output's own bf16 rounding) against
+    the oracle's FC2 and finalize on the GPU's own FC2 input, after the FC2
+    input itself is checked against the oracle. Nothing is re-taken. The
+    plain comparison with the oracle's own end-to-end result is returned
+    beside it (it differs only through FC2-input rounding decisions within
+    the FC1 accumulation allowance)."""
+    check_fc2_input(gi, ref, threads, what)
+    y_exp = expected_from_own_fc2_input(gi, ref, W, K, on_input, threads)
+    own = assert_output_close(y_gpu, y_exp, f"{what} (vs oracle FC2+finalize on the GPU's FC2 input)",
+                              round_allow)
+    plain = out_errors(y_gpu, ref["y"], round_allow)
+    print(f"{what}: vs own-FC2-input oracle max|err|/rms={own[0]:.3e} fro={own[1]:.3e}; "
+          f"vs end-to-end oracle max|err|/rms={plain[0]:.3e} fro={plain[1]:.3e}", flush=True)
+    return {"own": own, "plain": plain, "own_plain": out_errors(y_gpu, y_exp, False),
+            "plain_nr": out_errors(y_gpu, ref["y"], False)}
+
+
+def check_layer(moe, d, ws, y, ref, W, T: int, K: int, mode: str, on_input: bool, what="",
+                round_allow=False, threads: int = 8):
+    """check_layer_output on a forward's workspace and bf16 output tensor."""
+    gi = read_fc2_input(moe, d, ws, T, K, mode)
+    yg = bf16_to_f64(y)[ref["tokens"]]
+    return check_layer_output(yg, gi, ref, W, K, on_input, what, round_allow, threads)

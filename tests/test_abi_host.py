@@ -60,10 +60,10 @@ def test_workspace_grows_with_tokens(moe):
     assert 0 < a < b
 
 
-def _fwd(moe, d, prepared=FAKE, x=FAKE, logits=FAKE, T=16, K=2, mode=0, act=0, oni=0, det=1,
-         ws=FAKE, wsb=1 << 40, y=FAKE):
-    return moe._lib.moe_forward(ctypes.byref(d), prepared, x, logits, T, K, mode, act, oni, det,
-                                ws, wsb, y, None)
+def _fwd(moe, d, prepared=FAKE, pb=1 << 40, x=FAKE, logits=FAKE, T=16, K=2, mode=0, act=0, oni=0,
+         det=1, ws=FAKE, wsb=1 << 40, y=FAKE):
+    return moe._lib.moe_forward(ctypes.byref(d), prepared, pb, x, logits, T, K, mode, act, oni,
+                                det, ws, wsb, y, None)
 
 
 def test_forward_rejects_before_launch(moe):
@@ -81,6 +81,12 @@ def test_forward_rejects_before_launch(moe):
     assert _fwd(moe, d, ws=ctypes.c_void_p((1 << 20) + 16)) == 1  # workspace not 256-aligned
     assert _fwd(moe, d, wsb=1024) == 3                     # MOE_ERR_WORKSPACE
     assert "workspace" in moe._lib.moe_last_error().decode()
+    # a prepared blob smaller than these dimensions need (e.g. prepared for a
+    # smaller layer) is refused before anything could read past its end
+    need = moe._lib.moe_prepared_bytes(ctypes.byref(d))
+    assert _fwd(moe, d, pb=need - 1) == 3
+    assert "prepared blob" in moe._lib.moe_last_error().decode()
+    assert moe._lib.moe_forward_status(None, ctypes.byref(ctypes.c_int32()), None) == 1
     assert _fwd(moe, _dims(moe, H=200)) == 2               # MOE_ERR_UNSUPPORTED
     big = _dims(moe, E=64, H=8192, I=2048)
     assert _fwd(moe, big, T=1 << 15, K=8) == 2              # activations of 4 GiB or more

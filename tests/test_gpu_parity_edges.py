@@ -13,8 +13,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import block_scaled_fp4_top_amd as moe  # noqa: E402
-from tests.helpers import (Inputs, assert_output_close, assert_output_close_flips,  # noqa: E402
-                           bf16_to_f64, check_fc2_input)
+from tests.helpers import Inputs, check_layer  # noqa: E402
 from tests.test_gpu_parity_small import check_routing, check_x_quant, run_layer  # noqa: E402
 
 
@@ -35,8 +34,7 @@ def _run_and_check(inp, K, mode, on_input, det=True, what=""):
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, inp.T, K, mode, ref)
     check_x_quant(d, ws, inp.T, K, mode, ref)
-    check_fc2_input(moe, d, ws, inp.T, K, mode, ref, what)
-    return assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what)
+    return check_layer(moe, d, ws, y, ref, W, inp.T, K, mode, on_input, what)
 
 
 @pytest.mark.parametrize("mode", ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"])
@@ -55,10 +53,10 @@ def test_k1_and_k_equals_e(mode):
 
 def test_many_empty_experts():
     inp = Inputs(8, 256, 128, 64, 2, "swiglu", "normal")
-    d, blob, ws, y, ref, _ = run_layer(inp, 2, "w4a16", False, True)
+    d, blob, ws, y, ref, W = run_layer(inp, 2, "w4a16", False, True)
     assert (ref["counts"] == 0).sum() >= 40
     check_routing(d, ws, 8, 2, "w4a16", ref)
-    assert_output_close(bf16_to_f64(y), ref["y"], "empty experts")
+    check_layer(moe, d, ws, y, ref, W, 8, 2, "w4a16", False, "empty experts")
 
 
 @pytest.mark.parametrize("mode", ["w4a4_tensor", "w4a16", "mxfp8"])
@@ -134,3 +132,25 @@ def test_invalid_arguments_rejected_before_launch():
     d2 = moe.Dims(8, 256, 256, "swiglu", "nvfp4")
     with pytest.raises(moe.MoeError):      # blob prepared for other dims
         moe.check_prepared(d2, blob)
+
+
+@pytest.mark.parametrize("det", [True, False])
+def test_mismatched_blob_header_detected_on_device(det):
+    """A blob prepared for other dimensions but large enough for the call (a
+    SwiGLU blob used as a ReLU2 one): the forward's first kernel finds the
+    header difference, no kernel writes y, and the status word says so; a
+    matching forward on the same workspace then reports 0."""
+    T, H, I, E, K = 16, 256, 128, 8, 2
+    inp = Inputs(T, H, I, E, K, "swiglu", "normal")
+    d_sw = moe.Dims(E, H, I, "swiglu", "nvfp4")
+    d_r2 = moe.Dims(E, H, I, "relu2", "nvfp4")
+    blob = moe.prepare_weights(d_sw, inp.w1, inp.w2)
+    assert blob.numel() >= moe.prepared_bytes(d_r2)
+    ws = torch.empty(moe.workspace_bytes(d_sw, T, K, "w4a4_tensor"), dtype=torch.uint8, device="cuda")
+    y = torch.full((T, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    moe.forward(d_r2, blob, inp.x, inp.logits, K, "w4a4_tensor", False, det, workspace=ws, out=y)
+    assert moe.forward_status(ws) == 1
+    assert bool((y == 3.0).all()), "y written although the blob header did not match"
+    moe.forward(d_sw, blob, inp.x, inp.logits, K, "w4a4_tensor", False, det, workspace=ws, out=y)
+    assert moe.forward_status(ws) == 0
+    assert not bool((y == 3.0).all())

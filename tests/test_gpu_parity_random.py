@@ -21,11 +21,11 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
-from tests.helpers import Inputs, assert_output_close_flips, bf16_to_f64, check_fc2_input  # noqa: E402
+from tests.helpers import Inputs, check_layer  # noqa: E402
 from tests.test_gpu_parity_small import check_routing, check_x_quant, run_layer  # noqa: E402
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 
-MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6"]
 
 
 def _cases(n=24, seed=20261202):
@@ -96,8 +96,7 @@ def test_random_shape(case):
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, T, K, mode, ref)
     check_x_quant(d, ws, T, K, mode, ref)
-    check_fc2_input(moe, d, ws, T, K, mode, ref, what)
-    assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input, what, round_allow=True)
+    check_layer(moe, d, ws, y, ref, W, T, K, mode, on_input, what, round_allow=True)
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -116,9 +115,9 @@ def test_workspace_reuse_across_shapes(mode):
     y_fresh = moe.forward(d, blob, small.x, small.logits, K, mode, True, True)
     torch.cuda.synchronize()
     assert torch.equal(y_reused.view(torch.int16), y_fresh.view(torch.int16)), f"{mode}: reused workspace differs"
-    _, _, _, y, ref, W = run_layer(small, K, mode, True, True)
+    _, _, ws2, y, ref, W = run_layer(small, K, mode, True, True)
     assert torch.equal(y.view(torch.int16), y_fresh.view(torch.int16))
-    assert_output_close_flips(bf16_to_f64(y_reused), ref, W, mode, K, True, f"reuse {mode}")
+    check_layer(moe, d, ws2, y_reused, ref, W, 37, K, mode, True, f"reuse {mode}")
 
 
 def test_concurrent_forwards_share_a_blob():

@@ -13,17 +13,16 @@ if not torch.cuda.is_available():  # collected on CPU runs too; every test is ma
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 from oracle import reference as R  # noqa: E402
 from tests.helpers import (Inputs, TOPW_REL, assert_output_close,  # noqa: E402
-                           assert_output_close_flips, bf16_to_f64, check_fc2_input,
-                           unpack_expert, unpack_nibbles)
+                           bf16_to_f64, check_layer, unpack_expert, unpack_nibbles)
 
-MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6"]
 
 
 def _fmt(mode):
     return "mxfp8" if mode == "mxfp8" else "nvfp4"
 
 
-def run_layer(inp: Inputs, K, mode, on_input, det, threads=8, tokens=None):
+def run_layer(inp: Inputs, K, mode, on_input, det, threads=8, tokens=None, batched=False):
     d = moe.Dims(inp.E, inp.H, inp.I, inp.act, _fmt(mode))
     blob = moe.prepare_weights(d, inp.w1, inp.w2)
     moe.check_prepared(d, blob)
@@ -32,7 +31,7 @@ def run_layer(inp: Inputs, K, mode, on_input, det, threads=8, tokens=None):
     torch.cuda.synchronize()
     W = inp.oracle_weights(_fmt(mode))
     ref = R.forward(inp.x_bits(), inp.logits_np(), W, K, mode, inp.act, on_input,
-                    tokens=tokens, threads=threads)
+                    tokens=tokens, threads=threads, batched=batched)
     return d, blob, ws, y, ref, W
 
 
@@ -63,7 +62,7 @@ def check_x_quant(d, ws, T, K, mode, ref):
     assert np.array_equal(codes, xq["codes"])
     assert np.array_equal(view(d, ws, T, K, mode, "x_scales").reshape(T, H // 16), xq["scales"])
     g = view(d, ws, T, K, mode, "x_g")
-    if mode == "w4a4_token":
+    if mode in R.PER_ROW_MODES:
         assert np.array_equal(g[:T], xq["g"])
     else:
         assert g[0] == xq["g"][0]
@@ -80,9 +79,7 @@ def test_tiny_layer(mode, act, on_input, det):
     d, blob, ws, y, ref, W = run_layer(inp, K, mode, on_input, det)
     check_routing(d, ws, T, K, mode, ref)
     check_x_quant(d, ws, T, K, mode, ref)
-    check_fc2_input(moe, d, ws, T, K, mode, ref, f"{mode}/{act}")
-    assert_output_close_flips(bf16_to_f64(y), ref, W, mode, K, on_input,
-                              f"{mode}/{act}/{on_input}/{det}")
+    check_layer(moe, d, ws, y, ref, W, T, K, mode, on_input, f"{mode}/{act}/{on_input}/{det}")
 
 
 @pytest.mark.parametrize("mode", MODES)
@@ -135,7 +132,7 @@ def _crafted_matrix(rows, cols, seed):
     return v
 
 
-@pytest.mark.parametrize("kind", ["nvfp4_tensor", "nvfp4_row", "mxfp8"])
+@pytest.mark.parametrize("kind", ["nvfp4_tensor", "nvfp4_row", "mxfp8", "nvfp4_row_4o6"])
 def test_quantizer_bit_exact(kind):
     # shapes reach every row-quantizer variant: few long rows (a block per
     # row, and rows split into chunks of 256 quantization blocks: 2 chunks for
@@ -153,7 +150,8 @@ def test_quantizer_bit_exact(kind):
             assert np.array_equal(codes.cpu().numpy(), oc)
             assert np.array_equal(scales.cpu().numpy(), osc)
         else:
-            oc, osf, og = R.nvfp4_quantize(vn, per_row=kind == "nvfp4_row")
+            oc, osf, og = R.nvfp4_quantize(vn, per_row=kind != "nvfp4_tensor",
+                                           four_over_six=kind == "nvfp4_row_4o6")
             assert np.array_equal(unpack_nibbles(codes.cpu().numpy(), cols), oc)
             assert np.array_equal(scales.cpu().numpy(), osf)
             assert np.array_equal(g.cpu().numpy(), og)

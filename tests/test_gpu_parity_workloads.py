@@ -1,10 +1,13 @@
-"""GPU parity at the five synthetic workloads' full sizes, in the launch
+"""GPU parity at the synthetic workloads' full sizes, in the launch
 configuration the benchmark times. Routing, permutation and the quantized
-FC1 input are compared bit-exactly in full; prepared weights on a sample of
-experts; the layer output on every token where the oracle can afford it
-(T <= 256) and on a seeded sample of tokens otherwise (their outputs do not
-depend on other tokens except through the per-tensor FC2-input scale, for
-which the oracle runs FC1 over every route)."""
+FC1 input are compared bit-exactly in full; the NVFP4 FC2-input quantizer
+bit-exactly on every route (given the GPU's own fp32 values); prepared
+weights on a sample of experts; the layer output on every token where T <=
+256, otherwise on a sample of tokens that holds the first and the last row
+of every expert with rows (so every expert's first and last, usually
+partial, M-tile) topped up at random to at least 256 tokens. A token's
+output does not depend on other tokens except through the per-tensor
+FC2-input scale, for which the oracle runs FC1 over every route."""
 import time
 
 import numpy as np
@@ -19,15 +22,34 @@ if not torch.cuda.is_available():
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 from oracle import reference as R  # noqa: E402
 from synth_inputs import WORKLOADS  # noqa: E402
-from tests.helpers import (Inputs, assert_output_close_flips, bf16_to_f64,  # noqa: E402
-                           check_fc2_input, unpack_expert)
+from tests.helpers import Inputs, check_layer, unpack_expert  # noqa: E402
 from tests.test_gpu_parity_small import check_routing, check_x_quant  # noqa: E402
 
 THREADS = 16
+MIN_SAMPLE = 256
 
 
 def _log(msg):
     print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+def sample_tokens(logits: np.ndarray, K: int, E: int, T: int, seed=1234):
+    """Tokens holding the first and the last row of every expert with rows,
+    plus random tokens up to MIN_SAMPLE (all tokens if T <= MIN_SAMPLE)."""
+    if T <= MIN_SAMPLE:
+        return None
+    ids, _ = R.route(logits, K)
+    counts, offsets, r2r, _ = R.permute(ids, E)
+    toks = set()
+    for e in range(E):
+        if counts[e]:
+            toks.add(int(r2r[offsets[e]]) // K)
+            toks.add(int(r2r[offsets[e + 1] - 1]) // K)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.array(sorted(toks)))
+    extra = max(0, MIN_SAMPLE - len(toks))
+    toks |= set(int(t) for t in rng.choice(rest, size=extra, replace=False))
+    return sorted(toks)
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -44,18 +66,18 @@ def test_workload_full_size(name):
         ys[fin] = moe.forward(d, blob, inp.x, inp.logits, wl.K, wl.mode, wl.on_input,
                               fin == "det", workspace=ws)
     torch.cuda.synchronize()
-    _log("forward done; oracle routing/permutation/quantization")
     W = inp.oracle_weights(wl.wfmt)
-    if wl.T <= 256:
-        tokens = None
-    else:
-        rng = np.random.default_rng(1234)
-        tokens = sorted(rng.choice(wl.T, size=8, replace=False).tolist())
-    ref = R.forward(inp.x_bits(), inp.logits_np(), W, wl.K, wl.mode, wl.act, wl.on_input,
-                    tokens=tokens, threads=THREADS)
+    logits = inp.logits_np()
+    tokens = sample_tokens(logits, wl.K, wl.E, wl.T)
+    ntok = wl.T if tokens is None else len(tokens)
+    _log(f"forward done; oracle on {ntok} tokens ({ntok * wl.K} routes)")
+    ref = R.forward(inp.x_bits(), logits, W, wl.K, wl.mode, wl.act, wl.on_input,
+                    tokens=tokens, threads=THREADS, batched=True)
     _log(f"oracle done ({len(W.q)} experts quantized)")
     check_routing(d, ws, wl.T, wl.K, wl.mode, ref)
     check_x_quant(d, ws, wl.T, wl.K, wl.mode, ref)
+    if tokens is not None:  # the sample reaches every expert with rows
+        assert set(ref["ids"][tokens].ravel().tolist()) == set(np.nonzero(ref["counts"])[0].tolist())
     # prepared weights: a few experts, including the most loaded one
     blob_np = blob.cpu().numpy()
     hot = int(np.argmax(ref["counts"]))
@@ -66,13 +88,19 @@ def test_workload_full_size(name):
         assert np.array_equal(w2c, oc2) and np.array_equal(w2s, os2), e
         if wl.wfmt == "nvfp4":
             assert g1 == og1 and g2 == og2
-    check_fc2_input(moe, d, ws, wl.T, wl.K, wl.mode, ref, name)
-    toks = ref["tokens"]
+    del blob_np
     for fin, y in ys.items():
-        yg = bf16_to_f64(y)[toks]
-        mx, fro = assert_output_close_flips(yg, ref, W, wl.mode, wl.K, wl.on_input,
-                                            f"{name} {fin}")
-        _log(f"{name} finalize={fin}: max|err|/rms={mx:.3e} rel_fro={fro:.3e}")
+        # the max bar counts the error beyond the output's own bf16 rounding:
+        # on these samples max|y| reaches 6-7 rms, where half a bf16 ulp
+        # alone is up to 2^-8 * |y| ~ 0.025 rms
+        res = check_layer(moe, d, ws, y, ref, W, wl.T, wl.K, wl.mode, wl.on_input,
+                          f"{name} {fin}", round_allow=True, threads=THREADS)
+        rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+        _log(f"{name} finalize={fin}: max|y|/rms={float(np.abs(ref['y']).max()) / rms:.2f}; "
+             f"vs oracle FC2+finalize on the GPU's FC2 input: max|err| beyond bf16 rounding/rms="
+             f"{res['own'][0]:.3e}, plain max|err|/rms={res['own_plain'][0]:.3e}, "
+             f"fro={res['own'][1]:.3e}; vs end-to-end oracle: plain max|err|/rms="
+             f"{res['plain_nr'][0]:.3e} fro={res['plain'][1]:.3e}")
     if "fused" in ys:
         # every token, not a sample: the fused output equals the deterministic
         # one up to the order of its fp32 atomic sums (one bf16 rounding step
