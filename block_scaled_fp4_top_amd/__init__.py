@@ -51,6 +51,7 @@ def _load():
         "moe_workspace_bytes": (sz, [D, i32, i32, i32]),
         "moe_forward": (ctypes.c_int, [D, P, sz, P, P, i32, i32, i32, i32, i32, i32, P, sz, P, P]),
         "moe_forward_status": (ctypes.c_int, [P, ctypes.POINTER(i32), P]),
+        "moe_forward_noalloc": (ctypes.c_int, [D, P, sz, P, P, i32, i32, i32, i32, i32, i32, P, P]),
         "moe_finalize": (ctypes.c_int, [P, i32, P, P, i32, i32, i32, P, P]),
         "moe_quantize": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P, P]),
         "moe_workspace_view": (ctypes.c_int, [D, i32, i32, i32, i32, ctypes.POINTER(sz),
@@ -68,7 +69,8 @@ def _load():
 
 _lib = _load()
 EXPORTS = ["moe_prepared_bytes", "moe_prepare_weights", "moe_check_prepared",
-           "moe_workspace_bytes", "moe_forward", "moe_forward_status", "moe_finalize", "moe_quantize",
+           "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_forward_status",
+           "moe_finalize", "moe_quantize",
            "moe_workspace_view", "moe_stage_timing", "moe_stage_times", "moe_last_error"]
 
 
@@ -182,6 +184,29 @@ def forward(d: Dims, blob: torch.Tensor, x: torch.Tensor, logits: torch.Tensor, 
                             MODES[mode], ACTS[d.act], int(bool(router_weight_on_input)),
                             int(bool(deterministic)), _ptr(workspace), workspace.numel(),
                             _ptr(out), ctypes.c_void_p(_stream(stream))))
+    return out
+
+
+def forward_noalloc(d: Dims, blob: torch.Tensor, x: torch.Tensor, logits: torch.Tensor, K: int,
+                    mode: str, router_weight_on_input: bool = False, deterministic: bool = True,
+                    out=None, stream=None) -> torch.Tensor:
+    """forward() on the library's built-in workspace (moe_forward_noalloc): no
+    workspace argument and no device allocation by the library. Forwards that
+    overlap in time on one GPU share that workspace and must not be run
+    concurrently. `out` (y, [T, H] bf16) is allocated here when not given."""
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[1] != d.H:
+        raise ValueError(f"x must be [T, {d.H}], got {tuple(x.shape)}")
+    T = x.shape[0]
+    _need(logits, "router_logits", torch.float32, (T, d.E), x.device)
+    _need(blob, "prepared", torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, d.H), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (T, d.H), x.device)
+    _check(_lib.moe_forward_noalloc(ctypes.byref(d.c()), _ptr(blob), blob.numel(), _ptr(x),
+                                    _ptr(logits), T, K, MODES[mode], ACTS[d.act],
+                                    int(bool(router_weight_on_input)), int(bool(deterministic)),
+                                    _ptr(out), ctypes.c_void_p(_stream(stream))))
     return out
 
 

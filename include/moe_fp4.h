@@ -133,6 +133,25 @@ int moe_forward(const moe_dims* d, const void* prepared, size_t prepared_bytes, 
                 int32_t router_weight_on_input, int32_t deterministic_finalize, void* workspace,
                 size_t workspace_bytes, uint16_t* y, hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The same forward, on a
+ * workspace that is a device array inside the library (64 MiB; each GPU the
+ * library runs on holds its own copy until the process ends) instead of a
+ * caller buffer; the caller still passes the inputs and y. Arguments, their
+ * checks and error codes as for moe_forward; a shape whose workspace
+ * (moe_workspace_bytes) exceeds 64 MiB returns MOE_ERR_WORKSPACE before any
+ * launch. No call allocates memory; the first call on a device looks up the
+ * array's device address (hipGetSymbolAddress) with that device current, so
+ * `stream` must belong to the current device. All calls on one GPU share the
+ * array, which keeps the last call's contents (every forward rewrites what it
+ * reads): forwards that overlap in time on one GPU, on different streams or
+ * host threads, race and must be serialised by the caller. The status word
+ * of the device-side blob check lives in that array and is not readable. */
+int moe_forward_noalloc(const moe_dims* d, const void* prepared, size_t prepared_bytes,
+                        const uint16_t* x, const float* logits, int32_t T, int32_t K,
+                        int32_t mode, int32_t act, int32_t router_weight_on_input,
+                        int32_t deterministic_finalize, uint16_t* y, hipStream_t stream);
+
 /* Status word of the last forward enqueued on `workspace` (synchronous: waits
  * for `stream`, then reads 4 bytes): *status = 0 after a forward whose blob
  * header matched its dimensions, MOE_ERR_INVALID otherwise (y was then not
