@@ -3,9 +3,10 @@
 Default (the headline line): the MXFP8 W8A8 prefill layer, T=16384 tokens,
 H=7168, I=2048, E=256 experts, top-8, SwiGLU, Zipf(1.1)-skewed routing, router
 weight on the output side, fused finalize (its configured variant); the
-deterministic finalize is timed beside it. The four other workloads (tiny
-NVFP4 W4A4, NVFP4 W4A16 decode, NVFP4 W4A4 per-token prefill, NVFP4 W4A4
-ReLU2 decode) follow as sub-records of the same line.
+deterministic finalize is timed beside it. The other workloads (tiny NVFP4
+W4A4, NVFP4 W4A16 decode, NVFP4 W4A4 per-token prefill, NVFP4 W4A4 ReLU2
+decode, and the prefill under the 4-over-6 contract and on MXFP4 re-blocked
+GEMMs) follow as sub-records of the same line.
 
 A step is one moe_forward (routing, permutation, activation quantization, FC1
 with fused activation, FC2-input quantization, FC2, finalize) over inputs
@@ -30,19 +31,27 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
+DTYPES = {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "w4a4_token_4o6": "f16",
+          "mxfp8": "fp8", "w4a4_token_mxfp4": "fp4"}
 METRIC = "MoE layer tokens/s on 1 MI355X; % MFMA peak (prefill), % HBM BW (decode)"
 MALL_BYTES = 256 << 20
 HEADLINE = "prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8"
 SUBRECORDS = ["tiny_w4a4_tensor_T16_H256_I128_E8_K2", "decode_w4a16_T256_H2048_I1024_E64_K6",
               "prefill_w4a4_token_T4096_H4096_I2048_E128_K8",
-              "decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8"]
+              "decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8",
+              # the prefill layer under the 4-over-6 activation contract, and with
+              # its GEMMs on MXFP4 re-blocked operands (FP4 matrix cores)
+              "prefill_w4a4_token4o6_T4096_H4096_I2048_E128_K8",
+              "prefill_w4a4_token_mxfp4_T4096_H4096_I2048_E128_K8"]
 # oracle sample per workload: tokens of a sub-batch that take about 10-30 s
 # of single-thread CPU time
 CPU_SAMPLE_TOKENS = {"tiny_w4a4_tensor_T16_H256_I128_E8_K2": 16,
                      "decode_w4a16_T256_H2048_I1024_E64_K6": 48,
                      "prefill_w4a4_token_T4096_H4096_I2048_E128_K8": 8,
                      "decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8": 8,
+                     "prefill_w4a4_token4o6_T4096_H4096_I2048_E128_K8": 8,
+                     "prefill_w4a4_token_mxfp4_T4096_H4096_I2048_E128_K8": 8,
                      "prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8": 3,
                      "ep8_share_mxfp8_zipf_T2048_H7168_I2048_E32_K8": 3}
 
@@ -55,6 +64,8 @@ def parse():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-subrecords", action="store_true",
                     help="time the headline workload only")
+    ap.add_argument("--only-configured", action="store_true",
+                    help="time only the workload's configured finalize variant (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="0 = per-workload default")
     ap.add_argument("--copies", type=int, default=0, help="prepared weight copies (0 = auto)")
@@ -68,6 +79,8 @@ def weight_bytes(d, wfmt):
     scale)."""
     if wfmt == "nvfp4":
         return (d.N1 * d.H // 2 + d.N1 * d.H // 16 + 4, d.H * d.I // 2 + d.H * d.I // 16 + 4)
+    if wfmt == "mxfp4":
+        return (d.N1 * d.H // 2 + d.N1 * d.H // 32 + 4, d.H * d.I // 2 + d.H * d.I // 32 + 4)
     return (d.N1 * d.H + d.N1 * d.H // 32, d.H * d.I + d.H * d.I // 32)
 
 
@@ -179,7 +192,7 @@ def roofline(wl, d, counts, st_us, decode):
     kbytes = touched * (b1 if kern == "fc1" else b2) + io
     kflops = 2.0 * R_ * (wl.N1 * wl.H if kern == "fc1" else wl.H * wl.I)
     us = st_us[kern]
-    dtype = {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "mxfp8": "fp8"}[wl.mode]
+    dtype = DTYPES[wl.mode]
     if decode:
         ach = kbytes / (us * 1e-6) / 1e9
         r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -233,8 +246,10 @@ def run_workload(name, args, with_cpu):
         moe.forward(d, blobs[i % copies], x, logits, wl.K, wl.mode, wl.on_input, det,
                     workspace=ws, out=y)
 
+    conf = "fused" if wl.finalize == ("fused",) else "det"   # the configured variant
+    other = "det" if conf == "fused" else "fused"
     variants = {}
-    for fin in ("fused", "det"):
+    for fin in ((conf,) if args.only_configured else (conf, other)):
         det = fin == "det"
         # eager pass: per-stage HIP events on the launch stream (the GEMMs'
         # events are recorded at their own start and end)
@@ -289,8 +304,6 @@ def run_workload(name, args, with_cpu):
     counts = moe.workspace_view(d, ws, wl.T, wl.K, wl.mode, "counts").cpu().numpy()
     touched = int((counts > 0).sum())
     b1, b2 = weight_bytes(d, wl.wfmt)
-    conf = "fused" if wl.finalize == ("fused",) else "det"   # the configured variant
-    other = "det" if conf == "fused" else "fused"
     decode = wl.T <= 1024
     R_ = wl.T * wl.K
     flops = 2.0 * R_ * (wl.N1 * wl.H + wl.H * wl.I)
@@ -298,7 +311,7 @@ def run_workload(name, args, with_cpu):
     rec = {
         "value": round(wl.T / (v["ms"] * 1e-3), 1),
         "ms_per_step": round(v["ms"], 5),
-        "dtype": {"w4a16": "bf16", "w4a4_tensor": "f16", "w4a4_token": "f16", "mxfp8": "fp8"}[wl.mode],
+        "dtype": DTYPES[wl.mode],
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "K": wl.K,
                    "mode": wl.mode, "act": wl.act, "router_weight_on_input": wl.on_input,
                    "finalize": "fused" if conf == "fused" else "deterministic",
@@ -311,12 +324,13 @@ def run_workload(name, args, with_cpu):
         "layer_weight_gbs": round(touched * (b1 + b2) / (v["ms"] * 1e-3) / 1e9, 1),
         "roofline": roofline(wl, d, counts, v["st_us"], decode),
     }
-    o = variants[other]
-    rec["deterministic_finalize" if other == "det" else "fused_finalize"] = {
-        "value": round(wl.T / (o["ms"] * 1e-3), 1), "ms_per_step": round(o["ms"], 5),
-        "graph_step_ms_percentiles": o["pct"],
-        "stages_us": {k: round(u, 2) for k, u in o["st_us"].items()},
-        "roofline": roofline(wl, d, counts, o["st_us"], decode)}
+    if other in variants:
+        o = variants[other]
+        rec["deterministic_finalize" if other == "det" else "fused_finalize"] = {
+            "value": round(wl.T / (o["ms"] * 1e-3), 1), "ms_per_step": round(o["ms"], 5),
+            "graph_step_ms_percentiles": o["pct"],
+            "stages_us": {k: round(u, 2) for k, u in o["st_us"].items()},
+            "roofline": roofline(wl, d, counts, o["st_us"], decode)}
     rec["cpu_baseline"] = None
     if cpu_w is not None:
         n = args.cpu_sample_tokens or CPU_SAMPLE_TOKENS.get(wl.name, 8)

@@ -16,12 +16,14 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libmoe_fp4.so")
 
-MODES = {"w4a4_tensor": 0, "w4a4_token": 1, "w4a16": 2, "mxfp8": 3, "w4a4_token_4o6": 4}
+MODES = {"w4a4_tensor": 0, "w4a4_token": 1, "w4a16": 2, "mxfp8": 3, "w4a4_token_4o6": 4,
+         "w4a4_token_mxfp4": 5}
 ACTS = {"swiglu": 0, "relu2": 1}
-WFMTS = {"nvfp4": 0, "mxfp8": 1}
+WFMTS = {"nvfp4": 0, "mxfp8": 1, "mxfp4": 2}
 VIEWS = {"topk_ids": 0, "topk_w": 1, "counts": 2, "offsets": 3, "row_to_route": 4,
          "route_to_row": 5, "x_codes": 6, "x_scales": 7, "x_g": 8, "a2_pre": 9,
-         "a2_codes": 10, "a2_scales": 11, "a2_g": 12, "o": 13}
+         "a2_codes": 10, "a2_scales": 11, "a2_g": 12, "o": 13, "x_mx_codes": 14,
+         "x_mx_scales": 15, "a2_mx_codes": 16, "a2_mx_scales": 17}
 STAGES = ["route", "permute", "quantize_x", "fc1", "quantize_fc2_input", "fc2", "finalize"]
 
 
@@ -266,7 +268,7 @@ def quantize(v: torch.Tensor, kind: str, stream=None):
 _VIEW_DTYPES = {0: torch.int32, 1: torch.float32, 2: torch.int32, 3: torch.int32,
                 4: torch.int32, 5: torch.int32, 6: torch.uint8, 7: torch.uint8,
                 8: torch.float32, 10: torch.uint8, 11: torch.uint8, 12: torch.float32,
-                13: torch.float32}
+                13: torch.float32, 14: torch.uint8, 15: torch.uint8, 16: torch.uint8, 17: torch.uint8}
 
 
 def workspace_view(d: Dims, workspace: torch.Tensor, T: int, K: int, mode: str, view: str):

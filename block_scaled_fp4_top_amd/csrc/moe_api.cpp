@@ -55,7 +55,7 @@ static int check_dims(const moe_dims* d) {
     if (d->H <= 0 || d->I <= 0) return fail(MOE_ERR_INVALID, "H=%d, I=%d must be positive", d->H, d->I);
     if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_RELU2)
         return fail(MOE_ERR_INVALID, "act=%d is not a moe_act", d->act);
-    if (d->wfmt != MOE_FMT_NVFP4 && d->wfmt != MOE_FMT_MXFP8)
+    if (d->wfmt != MOE_FMT_NVFP4 && d->wfmt != MOE_FMT_MXFP8 && d->wfmt != MOE_FMT_MXFP4)
         return fail(MOE_ERR_INVALID, "wfmt=%d is not a moe_wfmt", d->wfmt);
     if (d->H % kTileK || d->I % kTileK)
         return fail(MOE_ERR_UNSUPPORTED, "H=%d and I=%d must be multiples of %d", d->H, d->I, kTileK);
@@ -92,13 +92,16 @@ extern "C" int moe_prepare_weights(const moe_dims* d, const float* w1, const flo
     float* g2 = reinterpret_cast<float*>(b + L.h.off_g2);
     const int swI = d->act == MOE_ACT_SWIGLU ? I : 0;
     HIP_TRY(launch_write_header(L.h, b, stream), "write header");
-    if (d->wfmt == MOE_FMT_NVFP4) {
+    if (d->wfmt == MOE_FMT_NVFP4 || d->wfmt == MOE_FMT_MXFP4) {
+        const bool mx4 = d->wfmt == MOE_FMT_MXFP4;
         HIP_TRY(launch_fill_u32(amax, 2 * (size_t)E, 0u, stream), "prepare zero");
         HIP_TRY(launch_prep_amax(w1, E, (size_t)N1 * H, amax, stream), "prepare amax W1");
         HIP_TRY(launch_prep_amax(w2, E, (size_t)H * I, amax + E, stream), "prepare amax W2");
-        HIP_TRY(launch_prep_nvfp4(w1, E, N1, H, swI, amax, g1, b + L.h.off_w1, b + L.h.off_s1, stream),
+        HIP_TRY((mx4 ? launch_prep_mxfp4 : launch_prep_nvfp4)(w1, E, N1, H, swI, amax, g1, b + L.h.off_w1,
+                                                             b + L.h.off_s1, stream),
                 "prepare W1");
-        HIP_TRY(launch_prep_nvfp4(w2, E, H, I, 0, amax + E, g2, b + L.h.off_w2, b + L.h.off_s2, stream),
+        HIP_TRY((mx4 ? launch_prep_mxfp4 : launch_prep_nvfp4)(w2, E, H, I, 0, amax + E, g2, b + L.h.off_w2,
+                                                             b + L.h.off_s2, stream),
                 "prepare W2");
     } else {
         HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(g1), (size_t)E, 0x3F800000u, stream), "g1");
@@ -125,7 +128,7 @@ extern "C" int moe_check_prepared(const moe_dims* d, const void* prepared, hipSt
 }
 
 static int check_mode(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
-    if (mode < MOE_W4A4_TENSOR || mode > MOE_W4A4_TOKEN_4O6)
+    if (mode < MOE_W4A4_TENSOR || mode > MOE_W4A4_TOKEN_MXFP4)
         return fail(MOE_ERR_INVALID, "mode=%d is not a moe_mode", mode);
     if (T < 1) return fail(MOE_ERR_INVALID, "T=%d must be >= 1", T);
     if (K < 1 || K > d->E || K > kMaxK) return fail(MOE_ERR_INVALID, "K=%d outside [1, min(E=%d, %d)]", K, d->E, kMaxK);
@@ -135,9 +138,11 @@ static int check_mode(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
     if ((long long)T * K * widest * 2 >= (1LL << 32))
         return fail(MOE_ERR_UNSUPPORTED, "T*K*max(H, I)*2 = %lld bytes of activations: 4 GiB or more",
                     (long long)T * K * widest * 2);
-    const bool want_f8 = mode == MOE_MXFP8;
-    if (want_f8 != (d->wfmt == MOE_FMT_MXFP8))
-        return fail(MOE_ERR_INVALID, "mode %d needs a %s weight blob", mode, want_f8 ? "MXFP8" : "NVFP4");
+    const int want = mode == MOE_MXFP8 ? MOE_FMT_MXFP8
+                     : (mode == MOE_W4A4_TOKEN_MXFP4 ? MOE_FMT_MXFP4 : MOE_FMT_NVFP4);
+    if (d->wfmt != want)
+        return fail(MOE_ERR_INVALID, "mode %d needs a %s weight blob", mode,
+                    want == MOE_FMT_MXFP8 ? "MXFP8" : (want == MOE_FMT_MXFP4 ? "MXFP4" : "NVFP4"));
     return MOE_OK;
 }
 
@@ -361,9 +366,10 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     int32_t* bhist = WS(int32_t, V_BHIST);
     int32_t* bbase = bhist + (size_t)P.nblk * E;
     uint32_t* misc = WS(uint32_t, V_MISC);
-    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
+    const bool mx4 = mode == MOE_W4A4_TOKEN_MXFP4;  // NVFP4 re-blocked to MXFP4 for the GEMMs
+    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6 || mx4;
     const bool f8 = mode == MOE_MXFP8;
-    const bool per_row = mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
+    const bool per_row = mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6 || mx4;
     const int qkind = mode == MOE_W4A4_TOKEN_4O6 ? QK_NV_ROW_4O6 : (per_row ? QK_NV_ROW : QK_NV_TENSOR);
     const bool fused = deterministic_finalize == 0;
     uint32_t* status = reinterpret_cast<uint32_t*>(ws);
@@ -389,8 +395,12 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
                     "x amax");
         HIP_TRY(launch_quant_rows(x, 1, T, H, qkind, misc + kMiscXAmax, kAmaxSlots, kAmaxStride,
                                   WS(uint8_t, V_XCODES), WS(uint8_t, V_XSCALES), WS(float, V_XG),
-                                  WS(uint16_t, V_XDEQ), stream),
+                                  mx4 ? nullptr : WS(uint16_t, V_XDEQ), stream),
                 "quantize x");
+        if (mx4)
+            HIP_TRY(launch_reblock_mxfp4(WS(uint8_t, V_XCODES), WS(uint8_t, V_XSCALES), (size_t)T * H,
+                                         WS(uint8_t, V_XMXCODES), WS(uint8_t, V_XMXSCALES), nullptr, stream),
+                    "re-block x");
     } else if (f8) {
         HIP_TRY(launch_quant_rows(x, 1, T, H, QK_MX, nullptr, 0, 0, WS(uint8_t, V_XCODES),
                                   WS(uint8_t, V_XSCALES), nullptr, nullptr, stream),
@@ -401,12 +411,13 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     const int BM = bm_of(bmi);
     const int mt_max = (R + BM - 1) / BM + E;
     const int32_t* tl = tiles + (size_t)bmi * (E + 1);
-    const int ab = nv4 ? AB_F16_NV : (f8 ? AB_FP8 : AB_BF16_NV);
+    const int ab = mx4 ? AB_FP4 : (nv4 ? AB_F16_NV : (f8 ? AB_FP8 : AB_BF16_NV));
 
     GemmArgs g1;
     memset(&g1, 0, sizeof g1);
-    g1.a = nv4 ? (const void*)WS(uint16_t, V_XDEQ) : (f8 ? (const void*)WS(uint8_t, V_XCODES) : (const void*)x);
-    g1.a_scales = f8 ? WS(uint8_t, V_XSCALES) : nullptr;
+    g1.a = mx4 ? (const void*)WS(uint8_t, V_XMXCODES)
+               : (nv4 ? (const void*)WS(uint16_t, V_XDEQ) : (f8 ? (const void*)WS(uint8_t, V_XCODES) : (const void*)x));
+    g1.a_scales = mx4 ? WS(uint8_t, V_XMXSCALES) : (f8 ? WS(uint8_t, V_XSCALES) : nullptr);
     g1.a_g = nv4 ? WS(float, V_XG) : nullptr;
     g1.a_g_per_row = per_row;
     g1.gather = 1;
@@ -442,15 +453,21 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     if (nv4) {
         HIP_TRY(launch_quant_rows(WS(float, V_A2F), 0, R, I, qkind,
                                   misc + kMiscA2Amax, kAmaxSlots, kAmaxStride, WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES),
-                                  WS(float, V_A2G), WS(uint16_t, V_A2DEQ), stream),
+                                  WS(float, V_A2G), mx4 ? nullptr : WS(uint16_t, V_A2DEQ), stream),
                 "quantize FC2 input");
+        if (mx4)
+            HIP_TRY(launch_reblock_mxfp4(WS(uint8_t, V_A2CODES), WS(uint8_t, V_A2SCALES), (size_t)R * I,
+                                         WS(uint8_t, V_A2MXCODES), WS(uint8_t, V_A2MXSCALES), status, stream),
+                    "re-block FC2 input");
     }
 
     if (fused) HIP_TRY(launch_fill_u32(WS(uint32_t, V_YACC), (size_t)T * H, 0u, stream), "zero y_acc");
     GemmArgs g2;
     memset(&g2, 0, sizeof g2);
-    g2.a = nv4 ? (const void*)WS(uint16_t, V_A2DEQ) : (f8 ? (const void*)WS(uint8_t, V_A2CODES) : (const void*)WS(uint16_t, V_A2F));
-    g2.a_scales = f8 ? WS(uint8_t, V_A2SCALES) : nullptr;
+    g2.a = mx4 ? (const void*)WS(uint8_t, V_A2MXCODES)
+               : (nv4 ? (const void*)WS(uint16_t, V_A2DEQ)
+                      : (f8 ? (const void*)WS(uint8_t, V_A2CODES) : (const void*)WS(uint16_t, V_A2F)));
+    g2.a_scales = mx4 ? WS(uint8_t, V_A2MXSCALES) : (f8 ? WS(uint8_t, V_A2SCALES) : nullptr);
     g2.a_g = nv4 ? WS(float, V_A2G) : nullptr;
     g2.a_g_per_row = per_row;
     g2.gather = 0;

@@ -232,12 +232,14 @@ __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "m
 template <int AB, int BM, int WN, int EPI, int P, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     constexpr bool F8 = AB == AB_FP8;
-    constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
+    constexpr bool F4 = AB == AB_FP4;
+    constexpr bool SC = F8 || F4;  // block-scaled matrix core (E8M0 scale per 32)
+    constexpr int A_ROW = F8 ? 128 : (F4 ? 64 : 256);  // bytes of one A row per K step
     constexpr int A_TILE = BM * A_ROW;
     __shared__ __attribute__((aligned(1024))) uint8_t sA[P][A_TILE];
-    // A scales (fp8): one wave-wide 4-byte direct load per step writes 64
+    // A scales (fp8, fp4): one wave-wide 4-byte direct load per step writes 64
     // words, so each buffer holds at least 64 rows' words even for BM < 64.
-    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][F8 ? (BM > 64 ? BM : 64) : 1];
+    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][SC ? (BM > 64 ? BM : 64) : 1];
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
     __shared__ int s_arow[BM];
 
@@ -328,12 +330,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     auto body = [&](auto ms_tag) {
         constexpr int MS = decltype(ms_tag)::value;
         constexpr bool BF = AB == AB_BF16_NV;
-        constexpr int A_ROW = F8 ? 128 : 256;            // bytes of one A row per K step
         const int KT = p.Kdim / kTileK;
         const size_t tiles_e = (size_t)(p.N / kStrip) * KT;
         const int gs0 = nb * (NW * WN) + wave * WN;  // first global strip of this wave
         const uint8_t* abase = static_cast<const uint8_t*>(p.a);
-        const size_t a_row_bytes = (size_t)p.Kdim * (F8 ? 1 : 2);
+        const size_t a_row_bytes = F4 ? (size_t)p.Kdim / 2 : (size_t)p.Kdim * (F8 ? 1 : 2);
         const int r_any = s_arow[0];                 // rows past the group re-read a valid row
 
         // A staging: every 1 KB of the LDS tile is one wave-wide direct load
@@ -349,8 +350,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         //  fp8: block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
         //    k = 64 h + 16 (l'/16) + [0, 16), the operand's own order (the
         //    128-byte-row form measured 3 % slower here).
+        //  fp4: block blk = ms holds lane l' = row ms*16 + l'%16, packed
+        //    k = 32 (l'/16) + [0, 32) (bytes 16 (l'/16) + [0, 16) of the row's
+        //    64-byte step): the lane's 32 values are the one 32-block whose
+        //    E8M0 scale that lane supplies (probed on gfx950).
         // Wave w loads the blocks w, w + NW, w + 2 NW, ...
-        constexpr int JB = F8 ? 2 : 4;
+        constexpr int JB = F8 ? 2 : (F4 ? 1 : 4);
         constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
         uint32_t aoff[AB_PER_WAVE];  // byte offset of the lane's A row chunk (A < 4 GiB)
         int adst[AB_PER_WAVE];
@@ -359,22 +364,23 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
             const int blk = wave + NW * i;
             const int ms = blk / JB, g = blk & 1, h = (blk % JB) >> 1;
             const int r8 = lane >> 3;  // row within the 8-row half
-            const int koff = F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ (7 * g)) << 4);
+            const int koff = F4 ? 16 * (lane >> 4)
+                                : (F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ (7 * g)) << 4));
             int r = r_any;
             if (ms < MS) {
-                const int rr = s_arow[ms * 16 + (F8 ? (lane & 15) : 8 * g + r8)];
+                const int rr = s_arow[ms * 16 + (SC ? (lane & 15) : 8 * g + r8)];
                 r = rr >= 0 ? rr : r_any;
             }
             aoff[i] = (uint32_t)((size_t)r * a_row_bytes + koff);
             adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
         }
         const uint8_t* ascsrc = nullptr;
-        if (F8) {
+        if (SC) {
             const int m = wave * 64 + lane;
             const int rr = m < MS * 16 ? s_arow[m] : -1;
             ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
         }
-        constexpr int L = AB_PER_WAVE + (F8 ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
+        constexpr int L = AB_PER_WAVE + (SC ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
 
         // Weight loads: small M tiles read each weight once, so they stream past
     // the caches (non-temporal); wide tiles rely on L2 hits across the M-tiles
@@ -390,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int i = 0; i < AB_PER_WAVE; ++i)
                 lds_load16(abase + aoff[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
-            if (F8) lds_load4(ascsrc + kk * 4, (real && wave * 64 < MS * 16) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
+            if (SC) lds_load4(ascsrc + kk * 4, (real && wave * 64 < MS * 16) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
                 const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
@@ -399,6 +405,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     c1[s] = load_b(q);
                     c2[s] = load_b(q + 1);
                     sc[s] = p.b_scales[tile * kF8TileScale + lane];
+                } else if (F4) {
+                    c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kF4TileBytes + lane * 16));
+                    sc[s] = p.b_scales[tile * kF4TileScale + lane];
                 } else {
                     c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16));
                     sc[s] = *reinterpret_cast<const uint32_t*>(
@@ -419,7 +428,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         const int a_slot0 = a_g * 1024 + a_r7 * 128 + (((lane >> 4) ^ a_r7 ^ (7 * a_g)) << 4);
         const int a_slot1 = a_slot0 ^ 64;
         auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
-            if (F8) {
+            if (F4) {
+                // E2M1 operands, four VGPRs each (the instruction reads no more
+                // for fp4), E8M0 scales of the lane's 32-block
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 1024 + lane * 16]);
+                    const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+                    const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w, 0, 0, 0, 0};
+                        acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc[ms][s], 4, 4, 0, asc, 0, (int)bs[s]);
+                    }
+                }
+            } else if (F8) {
 #pragma unroll
                 for (int ms = 0; ms < MS; ++ms) {
                     const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + lane * 16]);
@@ -616,8 +640,9 @@ static hipError_t launch_bm(int bm_index, const GemmArgs& a, hipStream_t s, hipE
     // each A fragment read from LDS feeds four matrix-core operations; with
     // 512 columns per block, eight waves (two per SIMD) share one A tile,
     // which halves the A re-reads against 256-column blocks.
-    constexpr int PW = AB == AB_FP8 ? 3 : 4;   // pipeline depth, four-wave wide tiles
-    constexpr int PW8 = AB == AB_FP8 ? 3 : 2;  // eight waves: what fits in 256 registers
+    constexpr bool SCL = AB == AB_FP8 || AB == AB_FP4;
+    constexpr int PW = SCL ? 3 : 4;   // pipeline depth, four-wave wide tiles
+    constexpr int PW8 = SCL ? 3 : 2;  // eight waves: what fits in 256 registers
     // MXFP8 FC1 quantizes whole 32-column blocks in its epilogue: a wave must
     // own 32 consecutive FC2-input columns, i.e. four strips under SwiGLU
     // (2I is always a multiple of 256) and two under ReLU2.
@@ -657,6 +682,8 @@ hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStre
                                                : launch_bm<AB_F16_NV, EPI_FC2>(bm_index, a, s, t0, t1);
     if (ab == AB_BF16_NV) return epi == EPI_FC1 ? launch_bm<AB_BF16_NV, EPI_FC1>(bm_index, a, s, t0, t1)
                                                 : launch_bm<AB_BF16_NV, EPI_FC2>(bm_index, a, s, t0, t1);
+    if (ab == AB_FP4) return epi == EPI_FC1 ? launch_bm<AB_FP4, EPI_FC1>(bm_index, a, s, t0, t1)
+                                            : launch_bm<AB_FP4, EPI_FC2>(bm_index, a, s, t0, t1);
     return epi == EPI_FC1 ? launch_bm<AB_FP8, EPI_FC1>(bm_index, a, s, t0, t1)
                           : launch_bm<AB_FP8, EPI_FC2>(bm_index, a, s, t0, t1);
 }

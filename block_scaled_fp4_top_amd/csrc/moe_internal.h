@@ -22,6 +22,8 @@ constexpr int kNvTileBytes = 1024;  // NVFP4 codes of a 16 x 128 micro-tile
 constexpr int kNvTileScale = 128;   // its 16 x 8 E4M3 scales
 constexpr int kF8TileBytes = 2048;  // MXFP8 codes of a 16 x 128 micro-tile
 constexpr int kF8TileScale = 64;    // its 16 x 4 E8M0 scales
+constexpr int kF4TileBytes = 1024;  // MXFP4 codes of a 16 x 128 micro-tile
+constexpr int kF4TileScale = 64;    // its 16 x 4 E8M0 scales
 constexpr int kPermChunk = 1024;    // routes per block in the permutation kernels
 constexpr int kNumBM = 4;           // M-tile sizes with a device tile list
 __host__ __device__ constexpr int bm_of(int i) { return 16 << i; }  // 16, 32, 64, 128
@@ -79,8 +81,9 @@ inline bool make_blob_layout(const moe_dims& d, BlobLayout* L) {
     h.act = d.act;
     h.pad0 = 0;
     const bool nv = d.wfmt == MOE_FMT_NVFP4;
-    L->w_tile_bytes = nv ? kNvTileBytes : kF8TileBytes;
-    L->s_tile_bytes = nv ? kNvTileScale : kF8TileScale;
+    const bool mx4 = d.wfmt == MOE_FMT_MXFP4;
+    L->w_tile_bytes = nv ? kNvTileBytes : (mx4 ? kF4TileBytes : kF8TileBytes);
+    L->s_tile_bytes = nv ? kNvTileScale : (mx4 ? kF4TileScale : kF8TileScale);
     const size_t E = (size_t)d.E;
     const size_t t1 = (size_t)(h.N1 / kStrip) * (size_t)(d.H / kTileK);  // tiles per expert
     const size_t t2 = (size_t)(d.H / kStrip) * (size_t)(d.I / kTileK);
@@ -122,6 +125,7 @@ constexpr size_t kWsStatusBytes = 256;
 enum WsView {
     V_IDS = 0, V_TOPW, V_COUNTS, V_OFFSETS, V_R2R, V_RT2ROW,
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
+    V_XMXCODES, V_XMXSCALES, V_A2MXCODES, V_A2MXSCALES,  // MXFP4 re-blocked operands
     V_NUM_PUBLIC,
     V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_YACC, V_NUM
 };
@@ -135,7 +139,8 @@ struct WsPlan {
 
 inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p) {
     const size_t R = (size_t)T * K, E = (size_t)d.E, H = (size_t)d.H, I = (size_t)d.I;
-    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6;
+    const bool mx4 = mode == MOE_W4A4_TOKEN_MXFP4;
+    const bool nv4 = mode == MOE_W4A4_TENSOR || mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6 || mx4;
     const bool f8 = mode == MOE_MXFP8;
     p->nblk = (int)((R + kPermChunk - 1) / kPermChunk);
     for (int v = 0; v < V_NUM; ++v) p->bytes[v] = 0;
@@ -158,6 +163,13 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
         p->bytes[V_A2SCALES] = R * I / 16;
         p->bytes[V_A2G] = R * 4;
         p->bytes[V_A2DEQ] = R * I * 2;
+        if (mx4) {  // the GEMMs read the re-blocked MXFP4 operands, no fp16 copies
+            p->bytes[V_XDEQ] = p->bytes[V_A2DEQ] = 0;
+            p->bytes[V_XMXCODES] = (size_t)T * H / 2;
+            p->bytes[V_XMXSCALES] = (size_t)T * H / 32;
+            p->bytes[V_A2MXCODES] = R * I / 2;
+            p->bytes[V_A2MXSCALES] = R * I / 32;
+        }
     } else if (f8) {
         p->bytes[V_XCODES] = (size_t)T * H;
         p->bytes[V_XSCALES] = (size_t)T * H / 32;
@@ -377,6 +389,47 @@ __device__ __forceinline__ void nvfp4_block_4o6(const float* v, float g, uint32_
     packed[0] = four ? p4[0] : p6[0];
     packed[1] = four ? p4[1] : p6[1];
     *sf_out = four ? s4 : s6;
+}
+
+// Re-blocking of one NVFP4 32-element block (two 16-blocks: 16 bytes of packed
+// codes, two E4M3 scale codes) to MXFP4 (OCP MX v1.0 rule for E2M1 elements):
+// the local values w = E2M1(code) * E4M3(sf) (at most 6 significant bits: exact
+// in fp32), X = floor(log2 max|w|) - 2, codes E2M1_RNE(w * 2^-X) (exact
+// product; the hardware converter rounds to nearest even, saturates and keeps
+// the sign, also of zeros); an all-zero block gets X = -127 and sign-only
+// codes. Writes the 16 packed MXFP4 bytes and returns the E8M0 code X + 127.
+// The NVFP4 global scale is not involved (w spans [2^-10, 2688], so
+// X lies in [-12, 9]).
+__device__ __forceinline__ uint32_t mxfp4_reblock32(const uint32_t* nv /*[4]*/, uint32_t sf0,
+                                                    uint32_t sf1, uint32_t* mx /*[4]*/) {
+    float w[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e2m1x8_to_f32(nv[j], w + 8 * j);
+    const float s0 = e4m3_value(sf0), s1 = e4m3_value(sf1);
+    float ab = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        w[i] = __fmul_rn(w[i], i < 16 ? s0 : s1);
+        ab = fmaxf(ab, fabsf(w[i]));
+    }
+    if (ab == 0.0f) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = nv[j] & 0x88888888u;  // sign bits only
+        return 0;
+    }
+    const int X = floor_log2(ab) - 2;
+    const float inv = u2f((uint32_t)(127 - X) << 23);  // 2^-X
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t o = 0;
+        const float* u = w + 8 * j;
+        o = e2m1_pair<0>(o, __fmul_rn(u[0], inv), __fmul_rn(u[1], inv));
+        o = e2m1_pair<1>(o, __fmul_rn(u[2], inv), __fmul_rn(u[3], inv));
+        o = e2m1_pair<2>(o, __fmul_rn(u[4], inv), __fmul_rn(u[5], inv));
+        o = e2m1_pair<3>(o, __fmul_rn(u[6], inv), __fmul_rn(u[7], inv));
+        mx[j] = o;
+    }
+    return (uint32_t)(X + 127);
 }
 
 // MXFP8 quantization of one 32-element block (OCP MX v1.0 scale rule):

@@ -39,6 +39,11 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
                              const uint32_t* amax_slot, int amax_slots, int amax_stride, uint8_t* codes,
                              uint8_t* scales, float* g, uint16_t* deq, hipStream_t s);
 
+// NVFP4 (packed codes, E4M3 per 16) of n consecutive elements re-blocked to
+// MXFP4 (packed codes, E8M0 per 32); status: skip when it points to non-zero.
+hipError_t launch_reblock_mxfp4(const uint8_t* nv_codes, const uint8_t* nv_scales, size_t n,
+                                uint8_t* mx_codes, uint8_t* mx_scales, const uint32_t* status,
+                                hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // status: the forward's status word (skip all work when not 0), or null.
 hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, const uint32_t* status,
@@ -52,17 +57,22 @@ hipError_t launch_prep_amax(const float* w, int E, size_t per_expert, uint32_t* 
 hipError_t launch_prep_nvfp4(const float* w, int E, int N, int K, int swiglu_I,
                              const uint32_t* amax, float* g, uint8_t* codes, uint8_t* scales,
                              hipStream_t s);
+// NVFP4-quantized with the expert's global scale, then re-blocked to MXFP4.
+hipError_t launch_prep_mxfp4(const float* w, int E, int N, int K, int swiglu_I,
+                             const uint32_t* amax, float* g, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s);
 hipError_t launch_prep_mxfp8(const float* w, int E, int N, int K, int swiglu_I, uint8_t* codes,
                              uint8_t* scales, hipStream_t s);
 
 // Grouped GEMMs.
-enum GemmAB { AB_F16_NV = 0, AB_BF16_NV = 1, AB_FP8 = 2 };
+// AB_FP4: MXFP4 operands (re-blocked NVFP4) on the block-scaled matrix cores.
+enum GemmAB { AB_F16_NV = 0, AB_BF16_NV = 1, AB_FP8 = 2, AB_FP4 = 3 };
 enum GemmEpi { EPI_FC1 = 0, EPI_FC2 = 1 };
 
 struct GemmArgs {
     // A: activations. gather != 0: A row of permuted row r is row_to_route[r] / topk.
     const void* a;
-    const uint8_t* a_scales;  // MXFP8 E8M0 [rows][Kdim/32]
+    const uint8_t* a_scales;  // MXFP8 / MXFP4 E8M0 [rows][Kdim/32]
     const float* a_g;         // NVFP4 activation global scale(s), null for W4A16
     int a_g_per_row;
     int gather;

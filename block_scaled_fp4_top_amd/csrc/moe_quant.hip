@@ -178,6 +178,26 @@ __global__ __launch_bounds__(256) void quant_rows_nvrow_kernel(const void* __res
     }
 }
 
+// NVFP4 rows (packed codes [rows][cols/2], E4M3 scales [rows][cols/16]) re-blocked
+// to MXFP4 (packed codes [rows][cols/2], E8M0 scales [rows][cols/32]): one
+// thread per 32-element block (16-byte loads and stores).
+__global__ __launch_bounds__(256) void reblock_mxfp4_kernel(const uint8_t* __restrict__ nv_codes,
+                                                            const uint8_t* __restrict__ nv_scales,
+                                                            size_t nblocks, uint8_t* __restrict__ mx_codes,
+                                                            uint8_t* __restrict__ mx_scales,
+                                                            const uint32_t* __restrict__ status) {
+    if (status && *status) return;
+    for (size_t b = (size_t)blockIdx.x * 256 + threadIdx.x; b < nblocks; b += (size_t)gridDim.x * 256) {
+        const uint4 c = reinterpret_cast<const uint4*>(nv_codes)[b];
+        const uint32_t nv[4] = {c.x, c.y, c.z, c.w};
+        const uint16_t sc = reinterpret_cast<const uint16_t*>(nv_scales)[b];
+        uint32_t mx[4];
+        const uint32_t e8 = mxfp4_reblock32(nv, sc & 0xFFu, sc >> 8, mx);
+        reinterpret_cast<uint4*>(mx_codes)[b] = make_uint4(mx[0], mx[1], mx[2], mx[3]);
+        mx_scales[b] = (uint8_t)e8;
+    }
+}
+
 // Max |v| over n elements as fp32 bits (order-free atomicMax on non-negative
 // floats compared as unsigned integers). Block b folds its maximum into word
 // (b % nslots) * stride of slot: spreading the atomics over words on separate
@@ -387,6 +407,50 @@ __global__ __launch_bounds__(256) void prep_mxfp8_kernel(const float* __restrict
     scales[tile * kF8TileScale + (p & 15) + 16 * kb4] = (uint8_t)e8;
 }
 
+// One thread per (expert, prepared row, 32-block): the two 16-blocks NVFP4-
+// quantized with the expert's global scale (as prep_nvfp4_kernel), then
+// re-blocked to MXFP4 and stored in the fp4 micro-tile register image: lane
+// (p % 16) + 16 q of tile (p / 16, k / 128) holds row p's 32-block q of the
+// tile (16 packed bytes, even element in the low nibble), scale byte at the
+// same lane index.
+__global__ __launch_bounds__(256) void prep_mxfp4_kernel(const float* __restrict__ w, int E, int N,
+                                                         int K, int swiglu_I,
+                                                         const uint32_t* __restrict__ amax,
+                                                         float* __restrict__ gout,
+                                                         uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+    const int nkb = K / 32;
+    const size_t total = (size_t)E * N * nkb;
+    const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (id >= total) return;
+    const int e = (int)(id / ((size_t)N * nkb));
+    const int rem = (int)(id % ((size_t)N * nkb));
+    const int p = rem / nkb, kb = rem % nkb;
+    const float g = __fdiv_rn(u2f(amax[e]), 2688.0f);
+    if (p == 0 && kb == 0) gout[e] = g;
+    const int n = logical_row(p, swiglu_I);
+    const float4* src = reinterpret_cast<const float4*>(w + ((size_t)e * N + n) * K + (size_t)kb * 32);
+    uint32_t nv[4], sf[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 q = src[4 * h + i];
+            v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+        }
+        nvfp4_block(v, g, nv + 2 * h, sf + h);
+    }
+    uint32_t mx[4];
+    const uint32_t e8 = mxfp4_reblock32(nv, sf[0], sf[1], mx);
+    const int kt = (kb * 32) / kTileK, q = kb % 4;
+    const size_t tiles_e = (size_t)(N / kStrip) * (K / kTileK);
+    const size_t tile = (size_t)e * tiles_e + (size_t)(p / kStrip) * (K / kTileK) + kt;
+    const int lane = (p & 15) + 16 * q;
+    *reinterpret_cast<uint4*>(codes + tile * kF4TileBytes + lane * 16) = make_uint4(mx[0], mx[1], mx[2], mx[3]);
+    scales[tile * kF4TileScale + lane] = (uint8_t)e8;
+}
+
 __global__ void write_header_kernel(BlobHeader h, uint32_t* __restrict__ dst) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(&h);
     if (threadIdx.x < sizeof(BlobHeader) / 4) dst[threadIdx.x] = w[threadIdx.x];
@@ -457,6 +521,16 @@ hipError_t launch_quant_rows(const void* v, int in_bf16, int rows, int cols, int
     return hipGetLastError();
 }
 
+hipError_t launch_reblock_mxfp4(const uint8_t* nv_codes, const uint8_t* nv_scales, size_t n,
+                                uint8_t* mx_codes, uint8_t* mx_scales, const uint32_t* status,
+                                hipStream_t s) {
+    // n (elements) is a multiple of 32; codes 16-byte aligned
+    const size_t nb = n / 32;
+    hipLaunchKernelGGL(reblock_mxfp4_kernel, dim3(grid_for(nb, 8192)), dim3(256), 0, s, nv_codes, nv_scales,
+                       nb, mx_codes, mx_scales, status);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 8192)), dim3(256), 0, s, p, n, v);
     return hipGetLastError();
@@ -495,6 +569,15 @@ hipError_t launch_prep_nvfp4(const float* w, int E, int N, int K, int swiglu_I,
                              hipStream_t s) {
     const size_t total = (size_t)E * N * (K / 16);
     hipLaunchKernelGGL(prep_nvfp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       w, E, N, K, swiglu_I, amax, g, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_mxfp4(const float* w, int E, int N, int K, int swiglu_I,
+                             const uint32_t* amax, float* g, uint8_t* codes, uint8_t* scales,
+                             hipStream_t s) {
+    const size_t total = (size_t)E * N * (K / 32);
+    hipLaunchKernelGGL(prep_mxfp4_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
                        w, E, N, K, swiglu_I, amax, g, codes, scales);
     return hipGetLastError();
 }

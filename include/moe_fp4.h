@@ -58,11 +58,20 @@ typedef enum {
      * row, and per 16-block the block max mapped to 6 or to 4, whichever gives
      * the smaller sum of squared errors (fp64, element order; ties to 6). The
      * GEMMs consume the result like any NVFP4 operand. */
-    MOE_W4A4_TOKEN_4O6 = 4
+    MOE_W4A4_TOKEN_4O6 = 4,
+    /* NVFP4 W4A4 with per-token activation scales, GEMMs on the block-scaled
+     * FP4 matrix cores: both operands re-blocked from NVFP4 (E4M3 per 16) to
+     * MXFP4 (E8M0 per 32) by the OCP MX rule, which rounds each element a second
+     * time (about 11-12 % relative Frobenius difference per GEMM operand against
+     * the NVFP4 values); the FP32 global scales are applied in the epilogues.
+     * Opt-in, for callers that accept that error; needs an MOE_FMT_MXFP4 blob. */
+    MOE_W4A4_TOKEN_MXFP4 = 5
 } moe_mode;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
-typedef enum { MOE_FMT_NVFP4 = 0, MOE_FMT_MXFP8 = 1 } moe_wfmt;
+/* MOE_FMT_MXFP4: the weights NVFP4-quantized (per-expert FP32 global scale)
+ * and re-blocked to MXFP4, in the FP4 matrix-core layout (mode 5 only). */
+typedef enum { MOE_FMT_NVFP4 = 0, MOE_FMT_MXFP8 = 1, MOE_FMT_MXFP4 = 2 } moe_wfmt;
 
 typedef enum {
     MOE_OK = 0,
@@ -190,6 +199,8 @@ int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8
  *   9 FC2 input, fp32 before quantization [R][I] (W4A4) or bf16 (W4A16)
  *   10 FC2-input codes           11 FC2-input scales      12 FC2-input global scale(s)
  *   13 permuted FC2 output O [R][H] f32 (deterministic finalize)
+ *   14/15 x re-blocked to MXFP4: codes [T][H/2], E8M0 scales [T][H/32] (mode 5)
+ *   16/17 FC2 input re-blocked to MXFP4: codes [R][I/2], scales [R][I/32] (mode 5)
  * Returns MOE_ERR_INVALID for a view the mode does not produce. */
 int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32_t mode, int32_t view_id,
                        size_t* offset, size_t* bytes);

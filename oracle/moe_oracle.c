@@ -344,6 +344,55 @@ void orc_mxfp8_dequant(int n, const uint8_t* codes, const uint8_t* sc, double* o
 }
 
 /* ------------------------------------------------------------------------- */
+/* Re-blocking NVFP4 to MXFP4 (the other NVFP4 GEMM option: block-scaled FP4   */
+/* matrix units take E8M0 scales per 32 elements, NVFP4 has E4M3 per 16).      */
+/* The block-local NVFP4 value w = E2M1(code) * E4M3(sf) (at most 6            */
+/* significant bits, exact in fp64) of each 32-element block is re-quantized   */
+/* by the OCP MX v1.0 rule for E2M1 elements: shared exponent                 */
+/* X = floor(log2(block max)) - 2 (2 = exponent of E2M1's largest normal),     */
+/* clamped to [-127, 127], elements E2M1_RNE(w / 2^X) (exact quotient,         */
+/* saturating at 6, sign kept). An all-zero block gets X = -127 (code 0) and   */
+/* sign-only codes. The FP32 global scale is not part of the block and stays   */
+/* as it is. MXFP4 value: E2M1(code) * 2^X (* g).                              */
+/* ------------------------------------------------------------------------- */
+void orc_mxfp4_reblock(int n, const uint8_t* codes, const uint8_t* sf, uint8_t* mx_codes,
+                       uint8_t* mx_scales) {
+    for (int b = 0; b < n / 32; ++b) {
+        double w[32];
+        double amax = 0.0;
+        for (int i = 0; i < 32; ++i) {
+            int k = b * 32 + i;
+            w[i] = orc_e2m1_decode(codes[k]) * orc_e4m3_decode(sf[k / 16]);
+            if (fabs(w[i]) > amax) amax = fabs(w[i]);
+        }
+        int X;
+        if (amax == 0.0) {
+            X = -127;
+        } else {
+            int ex;
+            frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1) */
+            X = (ex - 1) - 2;
+            if (X < -127) X = -127;
+            if (X > 127) X = 127;
+        }
+        mx_scales[b] = (uint8_t)(X + 127);
+        for (int i = 0; i < 32; ++i) {
+            if (amax == 0.0) {
+                mx_codes[b * 32 + i] = (uint8_t)(codes[b * 32 + i] & 8);
+            } else {
+                /* w carries the NVFP4 code's sign, also for zeros (-0 -> 8) */
+                mx_codes[b * 32 + i] = (uint8_t)orc_e2m1_encode(ldexp(w[i], -X));
+            }
+        }
+    }
+}
+
+void orc_mxfp4_dequant(int n, const uint8_t* codes, const uint8_t* sc, double* out) {
+    for (int i = 0; i < n; ++i)
+        out[i] = orc_e2m1_decode(codes[i]) * orc_e8m0_decode(sc[i / 32]);
+}
+
+/* ------------------------------------------------------------------------- */
 /* Weights: one NVFP4 global scale per expert per matrix                       */
 /* ------------------------------------------------------------------------- */
 
@@ -372,6 +421,9 @@ static double weight_value(int fmt, int K, const uint8_t* codes, const uint8_t* 
     uint8_t c = codes[(size_t)n * K + k];
     if (fmt == ORC_FMT_NVFP4)
         return orc_e2m1_decode(c) * orc_e4m3_decode(scales[(size_t)n * (K / 16) + k / 16]) *
+               (double)g;
+    if (fmt == ORC_FMT_MXFP4)
+        return orc_e2m1_decode(c) * orc_e8m0_decode(scales[(size_t)n * (K / 32) + k / 32]) *
                (double)g;
     return orc_e4m3_decode(c) * orc_e8m0_decode(scales[(size_t)n * (K / 32) + k / 32]);
 }

@@ -10,6 +10,7 @@
 
 #define ORC_FMT_NVFP4 0
 #define ORC_FMT_MXFP8 1
+#define ORC_FMT_MXFP4 2 /* NVFP4 weights re-blocked to MXFP4, with the NVFP4 global scale */
 #define ORC_ACT_SWIGLU 0
 #define ORC_ACT_RELU2 1
 
@@ -31,6 +32,9 @@ void orc_nvfp4_quantize(int n, const float* v, float g, uint8_t* codes, uint8_t*
 float orc_nvfp4_global_scale_4o6(float amax);
 void orc_nvfp4_quantize_4o6(int n, const float* v, float g, uint8_t* codes, uint8_t* sf);
 void orc_nvfp4_dequant(int n, const uint8_t* codes, const uint8_t* sf, float g, double* out);
+void orc_mxfp4_reblock(int n, const uint8_t* codes, const uint8_t* sf, uint8_t* mx_codes,
+                       uint8_t* mx_scales);
+void orc_mxfp4_dequant(int n, const uint8_t* codes, const uint8_t* sc, double* out);
 void orc_mxfp8_quantize(int n, const float* v, uint8_t* codes, uint8_t* sc);
 void orc_mxfp8_dequant(int n, const uint8_t* codes, const uint8_t* sc, double* out);
 

@@ -33,11 +33,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 
-FMT_NVFP4, FMT_MXFP8 = 0, 1
+FMT_NVFP4, FMT_MXFP8, FMT_MXFP4 = 0, 1, 2
 ACT_SWIGLU, ACT_RELU2 = 0, 1
-MODES = ("w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6")
+MODES = ("w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6", "w4a4_token_mxfp4")
 # modes whose activations carry one NVFP4 global scale per row (token / route)
-PER_ROW_MODES = ("w4a4_token", "w4a4_token_4o6")
+PER_ROW_MODES = ("w4a4_token", "w4a4_token_4o6", "w4a4_token_mxfp4")
+
+
+def weight_format(mode: str) -> str:
+    """The prepared-weight format a mode consumes."""
+    return {"mxfp8": "mxfp8", "w4a4_token_mxfp4": "mxfp4"}.get(mode, "nvfp4")
 
 
 def build(force: bool = False) -> str:
@@ -73,6 +78,8 @@ def lib():
         L.orc_nvfp4_global_scale_4o6.restype = f; L.orc_nvfp4_global_scale_4o6.argtypes = [f]
         L.orc_nvfp4_quantize_4o6.restype = None; L.orc_nvfp4_quantize_4o6.argtypes = [i, P, f, P, P]
         L.orc_nvfp4_dequant.restype = None; L.orc_nvfp4_dequant.argtypes = [i, P, P, f, P]
+        L.orc_mxfp4_reblock.restype = None; L.orc_mxfp4_reblock.argtypes = [i, P, P, P, P]
+        L.orc_mxfp4_dequant.restype = None; L.orc_mxfp4_dequant.argtypes = [i, P, P, P]
         L.orc_mxfp8_quantize.restype = None; L.orc_mxfp8_quantize.argtypes = [i, P, P, P]
         L.orc_mxfp8_dequant.restype = None; L.orc_mxfp8_dequant.argtypes = [i, P, P, P]
         L.orc_quantize_weight.restype = None
@@ -193,6 +200,37 @@ def nvfp4_dequant(codes, sf, g, per_row: bool) -> np.ndarray:
     return out
 
 
+def mxfp4_reblock(codes: np.ndarray, sf: np.ndarray, threads: int = 1):
+    """NVFP4 rows (unpacked codes [rows, n], E4M3 scales [rows, n/16]) re-blocked
+    to MXFP4 (E2M1 codes [rows, n], E8M0 scales [rows, n/32]) by
+    orc_mxfp4_reblock; the global scales are not involved."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    sf = np.ascontiguousarray(sf, dtype=np.uint8)
+    rows, n = codes.shape
+    mc = np.empty((rows, n), np.uint8)
+    ms = np.empty((rows, n // 32), np.uint8)
+    L = lib()
+
+    def one(r):
+        L.orc_mxfp4_reblock(n, _p(codes[r]), _p(sf[r]), _p(mc[r]), _p(ms[r]))
+    _pmap(one, range(rows), threads)
+    return mc, ms
+
+
+def mxfp4_dequant(codes, sc, g=None, per_row: bool = True) -> np.ndarray:
+    """E2M1(code) * 2^X (* g per row or for all rows), fp64 (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(sc, dtype=np.uint8)
+    rows, n = codes.shape
+    out = np.empty((rows, n), np.float64)
+    L = lib()
+    for r in range(rows):
+        L.orc_mxfp4_dequant(n, _p(codes[r]), _p(sc[r]), _p(out[r]))
+        if g is not None:
+            out[r] *= float(g[r] if per_row else g[0])
+    return out
+
+
 def mxfp8_quantize(v: np.ndarray, threads: int = 1):
     v = np.ascontiguousarray(v, dtype=np.float32)
     rows, n = v.shape
@@ -228,7 +266,9 @@ class QuantWeights:
     are needed."""
 
     def __init__(self, fmt: str, E: int, H: int, I: int, act: str, provider):
-        self.fmt = FMT_MXFP8 if fmt == "mxfp8" else FMT_NVFP4
+        # "mxfp4": NVFP4 quantization (per-expert global scale), then each row
+        # re-blocked to MXFP4 (orc_mxfp4_reblock); the global scale is kept
+        self.fmt = {"mxfp8": FMT_MXFP8, "mxfp4": FMT_MXFP4}.get(fmt, FMT_NVFP4)
         self.E, self.H, self.I = E, H, I
         self.N1 = 2 * I if act == "swiglu" else I
         self.provider = provider
@@ -241,7 +281,10 @@ class QuantWeights:
         blk = 32 if self.fmt == FMT_MXFP8 else 16
         sc = np.empty((N, K // blk), np.uint8)
         g = ctypes.c_float(0.0)
-        lib().orc_quantize_weight(self.fmt, N, K, _p(w), _p(codes), _p(sc), ctypes.byref(g))
+        qfmt = FMT_MXFP8 if self.fmt == FMT_MXFP8 else FMT_NVFP4
+        lib().orc_quantize_weight(qfmt, N, K, _p(w), _p(codes), _p(sc), ctypes.byref(g))
+        if self.fmt == FMT_MXFP4:
+            codes, sc = mxfp4_reblock(codes, sc)
         return codes, sc, np.float32(g.value)
 
     def ensure(self, experts, threads: int = 1):
@@ -272,6 +315,8 @@ class QuantWeights:
         N = c.shape[0]
         if self.fmt == FMT_NVFP4:
             return nvfp4_dequant(c, s, np.array([g] * N, np.float32), per_row=True)
+        if self.fmt == FMT_MXFP4:
+            return mxfp4_dequant(c, s, np.array([g], np.float32), per_row=False)
         return mxfp8_dequant(c, s)
 
     def dequant(self, e):
@@ -305,6 +350,10 @@ def quantize_x(x_bits: np.ndarray, mode: str, threads: int = 1) -> dict:
                 "deq": lambda t: mxfp8_dequant(codes[t:t + 1], sc[t:t + 1])[0]}
     per_row = mode in PER_ROW_MODES
     codes, sf, g = nvfp4_quantize(x, per_row, threads, four_over_six=mode == "w4a4_token_4o6")
+    if mode == "w4a4_token_mxfp4":
+        mc, ms = mxfp4_reblock(codes, sf, threads)
+        return {"codes": codes, "scales": sf, "g": g, "mx_codes": mc, "mx_scales": ms,
+                "deq": lambda t: mxfp4_dequant(mc[t:t + 1], ms[t:t + 1], g[t:t + 1])[0]}
     return {"codes": codes, "scales": sf, "g": g,
             "deq": lambda t: nvfp4_dequant(codes[t:t + 1], sf[t:t + 1],
                                            g[t:t + 1] if per_row else g, per_row)[0]}
@@ -454,7 +503,12 @@ def forward(x_bits: np.ndarray, logits: np.ndarray, W: QuantWeights, K: int, mod
         per_row = mode in PER_ROW_MODES
         c2, s2, g2 = nvfp4_quantize(a32, per_row, threads, four_over_six=mode == "w4a4_token_4o6")
         out["a2q"] = {"codes": c2, "scales": s2, "g": g2}
-        a2 = nvfp4_dequant(c2, s2, g2, per_row)
+        if mode == "w4a4_token_mxfp4":
+            mc2, ms2 = mxfp4_reblock(c2, s2, threads)
+            out["a2q"].update(mx_codes=mc2, mx_scales=ms2)
+            a2 = mxfp4_dequant(mc2, ms2, g2, per_row)
+        else:
+            a2 = nvfp4_dequant(c2, s2, g2, per_row)
 
     # S6 + S7
     o, y = fc2_finalize(W, ids, p, K, on_input, toks, lambda r: a2[a_idx[r]], threads, batched)

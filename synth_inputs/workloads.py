@@ -18,6 +18,7 @@ class Workload:
     E: int
     K: int
     mode: str          # "w4a4_tensor" | "w4a4_token" | "w4a16" | "mxfp8" | "w4a4_token_4o6"
+    #                    | "w4a4_token_mxfp4"
     act: str           # "swiglu" | "relu2"
     on_input: bool     # router weight applied before FC2 (input side)
     finalize: tuple    # finalize variants exercised: ("det",), ("fused",), ("det", "fused")
@@ -34,7 +35,7 @@ class Workload:
 
     @property
     def wfmt(self) -> str:
-        return "mxfp8" if self.mode == "mxfp8" else "nvfp4"
+        return {"mxfp8": "mxfp8", "w4a4_token_mxfp4": "mxfp4"}.get(self.mode, "nvfp4")
 
 
 WORKLOADS = {
@@ -49,6 +50,10 @@ WORKLOADS = {
         # the same prefill layer under the 4-over-6 per-token activation contract
         Workload("prefill_w4a4_token4o6_T4096_H4096_I2048_E128_K8", 4096, 4096, 2048, 128, 8,
                  "w4a4_token_4o6", "swiglu", True, ("det", "fused"), "normal_bias"),
+        # the same prefill layer with both GEMMs on NVFP4 operands re-blocked to
+        # MXFP4 (the FP4 matrix cores; opt-in, adds a second rounding)
+        Workload("prefill_w4a4_token_mxfp4_T4096_H4096_I2048_E128_K8", 4096, 4096, 2048, 128, 8,
+                 "w4a4_token_mxfp4", "swiglu", True, ("det", "fused"), "normal_bias"),
         Workload("decode_w4a4_tensor_relu2_T64_H7168_I2048_E256_K8", 64, 7168, 2048, 256, 8,
                  "w4a4_tensor", "relu2", True, ("det",), "uniform"),
         Workload("prefill_mxfp8_zipf_T16384_H7168_I2048_E256_K8", 16384, 7168, 2048, 256, 8,

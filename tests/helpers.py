@@ -92,6 +92,7 @@ class Inputs:
         return self.w1[e].cpu().numpy(), self.w2[e].cpu().numpy()
 
     def oracle_weights(self, fmt):
+        """fmt: "nvfp4", "mxfp8" or "mxfp4" (R.weight_format(mode))."""
         return R.QuantWeights(fmt, self.E, self.H, self.I, self.act, self.provider)
 
 
@@ -172,12 +173,35 @@ def unpack_mxfp8_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: in
     return outl, scl
 
 
+def unpack_mxfp4_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: int, swiglu_I=0):
+    """MXFP4 micro-tiles: lane l = row (l % 16) + 16 q holds 16 bytes = the row's
+    32-block q of the tile (even element in the low nibble); scale byte l."""
+    NT, KT = N // 16, K // 128
+    t = codes_b.reshape(NT, KT, 4, 16, 16)          # tile, q, row, byte
+    nib = np.stack([t & 15, t >> 4], axis=-1).reshape(NT, KT, 4, 16, 32)
+    out = np.empty((N, K), np.uint8)
+    ov = out.reshape(NT, 16, KT, 128)
+    for q in range(4):
+        ov[:, :, :, 32 * q:32 * q + 32] = nib[:, :, q].transpose(0, 2, 1, 3)
+    s = scales_b.reshape(NT, KT, 4, 16)             # block, row
+    sc = np.empty((N, K // 32), np.uint8)
+    scv = sc.reshape(NT, 16, KT, 4)
+    for b in range(4):
+        scv[:, :, :, b] = s[:, :, b, :].transpose(0, 2, 1)
+    rows = _logical_rows(N, swiglu_I)
+    outl = np.empty_like(out)
+    scl = np.empty_like(sc)
+    outl[rows] = out
+    scl[rows] = sc
+    return outl, scl
+
+
 def unpack_expert(blob: np.ndarray, e: int):
     """(W1 codes, W1 scales, g1, W2 codes, W2 scales, g2) of expert e."""
     h = blob_header(blob)
     E, H, I, N1 = h["E"], h["H"], h["I"], h["N1"]
-    nv = h["wfmt"] == 0
-    tb, sb = (1024, 128) if nv else (2048, 64)
+    nv, mx4 = h["wfmt"] == 0, h["wfmt"] == 2
+    tb, sb = (1024, 128) if nv else ((1024, 64) if mx4 else (2048, 64))
     t1 = (N1 // 16) * (H // 128)
     t2 = (H // 16) * (I // 128)
     sw = I if h["act"] == 0 else 0
@@ -187,7 +211,7 @@ def unpack_expert(blob: np.ndarray, e: int):
     s2 = blob[h["off_s2"] + e * t2 * sb: h["off_s2"] + (e + 1) * t2 * sb]
     g1 = blob[h["off_g1"] + 4 * e: h["off_g1"] + 4 * e + 4].view(np.float32)[0]
     g2 = blob[h["off_g2"] + 4 * e: h["off_g2"] + 4 * e + 4].view(np.float32)[0]
-    unpack = unpack_nvfp4_matrix if nv else unpack_mxfp8_matrix
+    unpack = unpack_nvfp4_matrix if nv else (unpack_mxfp4_matrix if mx4 else unpack_mxfp8_matrix)
     w1c, w1s = unpack(c1, s1, N1, H, sw)
     w2c, w2s = unpack(c2, s2, H, I, 0)
     return w1c, w1s, g1, w2c, w2s, g2
@@ -208,7 +232,7 @@ def unpack_nibbles(packed: np.ndarray, n: int) -> np.ndarray:
 # inside each 128-deep instruction more coarsely (measured up to 7.4e-5), so
 # its bound is wider. Both bounds carry a margin over the measurements.
 TAU = {"w4a4_tensor": 2.0 ** -18, "w4a4_token": 2.0 ** -18, "w4a4_token_4o6": 2.0 ** -18,
-       "w4a16": 2.0 ** -18,
+       "w4a4_token_mxfp4": 2.0 ** -11, "w4a16": 2.0 ** -18,
        "mxfp8": 2.0 ** -11}
 
 
@@ -305,8 +329,10 @@ class Fc2Input:
     FC1 epilogue), `codes` unpacked one per byte, `scales`, and `g` ([1] per
     tensor or [R] per route, NVFP4 only)."""
 
-    def __init__(self, mode, pre=None, codes=None, scales=None, g=None):
+    def __init__(self, mode, pre=None, codes=None, scales=None, g=None, mx_codes=None,
+                 mx_scales=None):
         self.mode, self.pre, self.codes, self.scales, self.g = mode, pre, codes, scales, g
+        self.mx_codes, self.mx_scales = mx_codes, mx_scales   # MXFP4 re-blocked (mode 5)
 
     def dequant_row(self, row: int) -> np.ndarray:
         """The fp64 FC2 input row the GPU's FC2 consumed (its own codes)."""
@@ -315,6 +341,9 @@ class Fc2Input:
             return self.pre[row].astype(np.float64)
         if m == "mxfp8":
             return R.mxfp8_dequant(self.codes[row:row + 1], self.scales[row:row + 1])[0]
+        if m == "w4a4_token_mxfp4":
+            return R.mxfp4_dequant(self.mx_codes[row:row + 1], self.mx_scales[row:row + 1],
+                                   self.g[row:row + 1])[0]
         per_row = m in R.PER_ROW_MODES
         g = self.g[row:row + 1] if per_row else self.g[:1]
         return R.nvfp4_dequant(self.codes[row:row + 1], self.scales[row:row + 1], g,
@@ -332,10 +361,14 @@ def read_fc2_input(moe, d, ws, T: int, K: int, mode: str) -> Fc2Input:
     if mode == "mxfp8":
         return Fc2Input(mode, codes=v("a2_codes").reshape(R_, I),
                         scales=v("a2_scales").reshape(R_, I // 32))
-    return Fc2Input(mode, pre=v("a2_pre").reshape(R_, I),
-                    codes=unpack_nibbles(v("a2_codes"), I).reshape(R_, I),
-                    scales=v("a2_scales").reshape(R_, I // 16),
-                    g=v("a2_g")[:R_ if mode in R.PER_ROW_MODES else 1])
+    gi = Fc2Input(mode, pre=v("a2_pre").reshape(R_, I),
+                  codes=unpack_nibbles(v("a2_codes"), I).reshape(R_, I),
+                  scales=v("a2_scales").reshape(R_, I // 16),
+                  g=v("a2_g")[:R_ if mode in R.PER_ROW_MODES else 1])
+    if mode == "w4a4_token_mxfp4":
+        gi.mx_codes = unpack_nibbles(v("a2_mx_codes"), I).reshape(R_, I)
+        gi.mx_scales = v("a2_mx_scales").reshape(R_, I // 32)
+    return gi
 
 
 def check_s5_quantizer(gi: Fc2Input, threads: int = 1, what=""):
@@ -351,6 +384,11 @@ def check_s5_quantizer(gi: Fc2Input, threads: int = 1, what=""):
         f"{what}: {int((gi.scales != sf).sum())} FC2-input block scales differ from the oracle's quantizer"
     assert np.array_equal(gi.codes, codes), \
         f"{what}: {int((gi.codes != codes).sum())} FC2-input codes differ from the oracle's quantizer"
+    if gi.mode == "w4a4_token_mxfp4":  # the re-blocking of the GPU's own NVFP4, bit-exact
+        mc, ms = R.mxfp4_reblock(gi.codes, gi.scales, threads)
+        assert np.array_equal(gi.mx_scales, ms), f"{what}: re-blocked E8M0 scales differ"
+        assert np.array_equal(gi.mx_codes, mc), \
+            f"{what}: {int((gi.mx_codes != mc).sum())} re-blocked MXFP4 codes differ"
 
 
 def check_a2_nvfp4(gi: Fc2Input, ref: dict, what=""):

@@ -58,7 +58,7 @@ import torch  # noqa: E402
 from synth_inputs import make_expert_weights, make_logits, make_x  # noqa: E402
 from tests.helpers import Fc2Input, check_layer_output  # noqa: E402
 
-LAYER_MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6"]
+LAYER_MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6", "w4a4_token_mxfp4"]
 
 
 def _bf16(y):
@@ -69,7 +69,7 @@ def _layer(mode, on_input, T=12, H=256, I=128, E=4, K=2, seed=1):
     x = make_x(seed, T, H).view(torch.int16).numpy().view(np.uint16)
     lg = make_logits(seed, T, E, "normal").numpy()
     w1, w2 = make_expert_weights(seed, E, 2 * I, H, I)
-    W = R.QuantWeights("mxfp8" if mode == "mxfp8" else "nvfp4", E, H, I, "swiglu",
+    W = R.QuantWeights(R.weight_format(mode), E, H, I, "swiglu",
                        lambda e: (w1[e].numpy(), w2[e].numpy()))
     ref = R.forward(x, lg, W, K, mode, "swiglu", on_input)
     rt2row = ref["route_to_row"]
@@ -89,6 +89,8 @@ def _layer(mode, on_input, T=12, H=256, I=128, E=4, K=2, seed=1):
         g = ref["a2q"]["g"]
         gi = Fc2Input(mode, pre=perm(a32), codes=perm(ref["a2q"]["codes"]),
                       scales=perm(ref["a2q"]["scales"]), g=perm(g) if mode in R.PER_ROW_MODES else g)
+        if mode == "w4a4_token_mxfp4":
+            gi.mx_codes, gi.mx_scales = perm(ref["a2q"]["mx_codes"]), perm(ref["a2q"]["mx_scales"])
     return W, ref, gi, K
 
 
@@ -138,7 +140,8 @@ def test_layer_check_rejects_wrong_route_weight(mode):
         check_layer_output(y, gi, ref, W, K, False, "swapped weight")
 
 
-@pytest.mark.parametrize("mode", ["w4a4_tensor", "w4a4_token", "mxfp8", "w4a4_token_4o6"])
+@pytest.mark.parametrize("mode", ["w4a4_tensor", "w4a4_token", "mxfp8", "w4a4_token_4o6",
+                                  "w4a4_token_mxfp4"])
 @pytest.mark.parametrize("consistent", [False, True])
 def test_layer_check_rejects_wrong_fc2_input_code(mode, consistent):
     """One FC2-input code one step off (toward zero) in the largest element of
@@ -191,3 +194,17 @@ def test_nvfp4_code_check_alone(mode):
             g2.codes[row, j], g2.codes[row, j ^ 1] = b, a
         with pytest.raises(AssertionError):
             check_a2_nvfp4(g2, ref2, plant)
+
+
+def test_layer_check_rejects_wrong_reblocked_code():
+    """Mode 5: one re-blocked MXFP4 FC2-input code one step off (the NVFP4 codes
+    right), with the output recomputed from it."""
+    W, ref, gi, K = _layer("w4a4_token_mxfp4", False)
+    row = 7
+    j = int(np.argmax(np.abs(gi.dequant_row(row))))
+    gi.mx_codes[row, j] = (gi.mx_codes[row, j] & 8) | ((gi.mx_codes[row, j] & 7) - 1)
+    r = int(ref["row_to_route"][row])
+    o = ref["o"].copy()
+    o[r] = W.fc2_rows(int(ref["ids"].flat[r]), gi.dequant_row(row)[None])[0]
+    with pytest.raises(AssertionError):
+        check_layer_output(_bf16(_finalize(ref, o, K, False)), gi, ref, W, K, False, "wrong mx code")

@@ -24,8 +24,9 @@ if not torch.cuda.is_available():
 from tests.helpers import Inputs, check_layer  # noqa: E402
 from tests.test_gpu_parity_small import check_routing, check_x_quant, run_layer  # noqa: E402
 import block_scaled_fp4_top_amd as moe  # noqa: E402
+from oracle import reference as R  # noqa: E402
 
-MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6"]
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6", "w4a4_token_mxfp4"]
 
 
 def _cases(n=24, seed=20261202):
@@ -107,7 +108,7 @@ def test_workspace_reuse_across_shapes(mode):
     E, K, H, I = 24, 4, 256, 128
     big = Inputs(300, H, I, E, K, "swiglu", "zipf", seed=7)
     small = Inputs(37, H, I, E, K, "swiglu", "normal", seed=8)
-    d = moe.Dims(E, H, I, "swiglu", "mxfp8" if mode == "mxfp8" else "nvfp4")
+    d = moe.Dims(E, H, I, "swiglu", R.weight_format(mode))
     blob = moe.prepare_weights(d, small.w1, small.w2)
     ws = torch.empty(moe.workspace_bytes(d, 300, K, mode), dtype=torch.uint8, device="cuda")
     moe.forward(d, blob, big.x, big.logits, K, mode, True, True, workspace=ws)

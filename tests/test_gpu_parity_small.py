@@ -15,11 +15,11 @@ from oracle import reference as R  # noqa: E402
 from tests.helpers import (Inputs, TOPW_REL, assert_output_close,  # noqa: E402
                            bf16_to_f64, check_layer, unpack_expert, unpack_nibbles)
 
-MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6"]
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6", "w4a4_token_mxfp4"]
 
 
 def _fmt(mode):
-    return "mxfp8" if mode == "mxfp8" else "nvfp4"
+    return R.weight_format(mode)
 
 
 def run_layer(inp: Inputs, K, mode, on_input, det, threads=8, tokens=None, batched=False):
@@ -66,6 +66,11 @@ def check_x_quant(d, ws, T, K, mode, ref):
         assert np.array_equal(g[:T], xq["g"])
     else:
         assert g[0] == xq["g"][0]
+    if mode == "w4a4_token_mxfp4":  # the GEMM operand: x re-blocked to MXFP4
+        assert np.array_equal(unpack_nibbles(view(d, ws, T, K, mode, "x_mx_codes"), H).reshape(T, H),
+                              xq["mx_codes"])
+        assert np.array_equal(view(d, ws, T, K, mode, "x_mx_scales").reshape(T, H // 32),
+                              xq["mx_scales"])
 
 
 @pytest.mark.parametrize("mode", MODES)

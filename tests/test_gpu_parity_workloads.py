@@ -22,7 +22,7 @@ if not torch.cuda.is_available():
 import block_scaled_fp4_top_amd as moe  # noqa: E402
 from oracle import reference as R  # noqa: E402
 from synth_inputs import WORKLOADS  # noqa: E402
-from tests.helpers import Inputs, check_layer, unpack_expert  # noqa: E402
+from tests.helpers import Inputs, bf16_to_f64, check_layer, unpack_expert  # noqa: E402
 from tests.test_gpu_parity_small import check_routing, check_x_quant  # noqa: E402
 
 THREADS = 16
@@ -101,6 +101,19 @@ def test_workload_full_size(name):
              f"{res['own'][0]:.3e}, plain max|err|/rms={res['own_plain'][0]:.3e}, "
              f"fro={res['own'][1]:.3e}; vs end-to-end oracle: plain max|err|/rms="
              f"{res['plain_nr'][0]:.3e} fro={res['plain'][1]:.3e}")
+    if wl.mode == "w4a4_token_mxfp4":
+        # the error re-blocking adds, stated against the exact-NVFP4 layer (the
+        # same inputs and tokens in the per-token W4A4 mode)
+        W_nv = inp.oracle_weights("nvfp4")
+        ref_nv = R.forward(inp.x_bits(), logits, W_nv, wl.K, "w4a4_token", wl.act, wl.on_input,
+                           tokens=tokens, threads=THREADS, batched=True)
+        y_nv = ref_nv["y"]
+        rms = float(np.sqrt(np.mean(y_nv ** 2)))
+        for label, yy in (("oracle with re-blocking", ref["y"]),
+                          ("GPU mode 5", bf16_to_f64(ys["det"])[ref["tokens"]])):
+            fro = float(np.linalg.norm(yy - y_nv) / np.linalg.norm(y_nv))
+            _log(f"{name}: {label} vs exact-NVFP4 oracle: rel Frobenius={fro:.4f} "
+                 f"max|err|/rms={float(np.abs(yy - y_nv).max()) / rms:.3f}")
     if "fused" in ys:
         # every token, not a sample: the fused output equals the deterministic
         # one up to the order of its fp32 atomic sums (one bf16 rounding step

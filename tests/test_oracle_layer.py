@@ -22,7 +22,7 @@ import torch
 from oracle import reference as R
 from synth_inputs import make_expert_weights, make_logits, make_x
 
-MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8"]
+MODES = ["w4a4_tensor", "w4a4_token", "w4a16", "mxfp8", "w4a4_token_4o6", "w4a4_token_mxfp4"]
 
 
 def _setup(T=16, H=256, I=128, E=8, mode="w4a4_tensor", act="swiglu", seed=0, logits="normal"):
@@ -31,8 +31,7 @@ def _setup(T=16, H=256, I=128, E=8, mode="w4a4_tensor", act="swiglu", seed=0, lo
     lg = make_logits(seed, T, E, logits).numpy()
     w1, w2 = make_expert_weights(seed, E, N1, H, I)
     w1, w2 = w1.numpy(), w2.numpy()
-    W = R.QuantWeights("mxfp8" if mode == "mxfp8" else "nvfp4", E, H, I, act,
-                       lambda e: (w1[e], w2[e]))
+    W = R.QuantWeights(R.weight_format(mode), E, H, I, act, lambda e: (w1[e], w2[e]))
     return x, lg, W
 
 
@@ -61,9 +60,12 @@ def _dense(x, lg, W, K, mode, act, on_input):
     elif mode == "mxfp8":
         a2 = R.mxfp8_dequant(*R.mxfp8_quantize(a32))
     else:
-        per_row = mode == "w4a4_token"
-        c, s, g = R.nvfp4_quantize(a32, per_row)
-        a2 = R.nvfp4_dequant(c, s, g, per_row)
+        per_row = mode in R.PER_ROW_MODES
+        c, s, g = R.nvfp4_quantize(a32, per_row, four_over_six=mode == "w4a4_token_4o6")
+        if mode == "w4a4_token_mxfp4":
+            a2 = R.mxfp4_dequant(*R.mxfp4_reblock(c, s), g, per_row)
+        else:
+            a2 = R.nvfp4_dequant(c, s, g, per_row)
     y = np.zeros((T, x.shape[1]))
     for t in range(T):
         for k in range(K):

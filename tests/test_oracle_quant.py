@@ -239,3 +239,58 @@ def test_nvfp4_4o6_roundtrip_on_max_to_4_grid():
         assert gg[0] == np.float32(g)
         deq = R.nvfp4_dequant(c, s, gg, per_row=True)
         assert np.array_equal(deq, row.astype(np.float64))
+
+
+def test_mxfp4_reblock_golden_blocks():
+    """Re-blocking NVFP4 to MXFP4 on hand-chosen blocks (exact-rational
+    derivation, no oracle call): round trip, saturation, exact ties, zero
+    block with signed zeros."""
+    mk = _load_golden_script("make_mxfp4_reblock_case")
+    with open(os.path.join(GOLD, "mxfp4_reblock_blocks.json")) as f:
+        ex = json.load(f)
+    assert [[e["e8m0"], e["codes"]] for e in ex["expected"]] == mk.derive()
+    for blk, exp in zip(ex["blocks"], ex["expected"]):
+        codes = np.array(blk["codes"], np.uint8)[None]
+        sf = np.array(blk["scales"], np.uint8)[None]
+        mc, ms = R.mxfp4_reblock(codes, sf)
+        assert int(ms[0, 0]) == exp["e8m0"]
+        assert list(mc[0]) == exp["codes"]
+
+
+def test_mxfp4_reblock_matches_exact_derivation_and_bounds():
+    """Seeded NVFP4 rows re-blocked by the oracle equal the exact-rational
+    derivation block for block; each re-blocked value is within half the E2M1
+    gap at the block scale of the NVFP4 value (at most 2^X), or saturated
+    (at most 2 * 2^X), and the dequantized row is code * 2^X exactly."""
+    from fractions import Fraction as F
+    mk = _load_golden_script("make_mxfp4_reblock_case")
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal((5, 128)) * np.exp2(rng.integers(-4, 4, (5, 1)))).astype(np.float32)
+    codes, sf, g = R.nvfp4_quantize(v, per_row=True)
+    mc, ms = R.mxfp4_reblock(codes, sf)
+    for r in range(v.shape[0]):
+        for b in range(v.shape[1] // 32):
+            e8, cc = mk.reblock([int(c) for c in codes[r, 32 * b:32 * b + 32]],
+                                [int(s) for s in sf[r, 2 * b:2 * b + 2]])
+            assert int(ms[r, b]) == e8 and list(mc[r, 32 * b:32 * b + 32]) == cc
+    w = R.nvfp4_dequant(codes, sf, np.ones(5, np.float32), per_row=True)   # local values
+    rb = R.mxfp4_dequant(mc, ms)
+    scale = np.repeat(np.exp2(ms.astype(np.float64) - 127), 32, axis=1)
+    err = np.abs(rb - w)
+    assert np.all(err <= 2.0 * scale)
+    assert np.all(err[np.abs(w) <= 6.0 * scale] <= 1.0 * scale[np.abs(w) <= 6.0 * scale])
+
+
+def test_mxfp4_reblock_round_trip_on_power_of_two_scales():
+    """When both halves of every 32-block share one power-of-two E4M3 scale,
+    NVFP4 values are already MXFP4 values: re-blocking keeps every value."""
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, size=(3, 96)).astype(np.uint8)
+    sf = np.empty((3, 6), np.uint8)
+    for r in range(3):
+        for b in range(3):
+            e = int(rng.integers(1, 15))                # exponent field, mantissa 0
+            sf[r, 2 * b] = sf[r, 2 * b + 1] = e << 3
+    w = R.nvfp4_dequant(codes, sf, np.ones(3, np.float32), per_row=True)
+    mc, ms = R.mxfp4_reblock(codes, sf)
+    assert np.array_equal(R.mxfp4_dequant(mc, ms), w)
