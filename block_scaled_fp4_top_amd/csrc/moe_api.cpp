@@ -173,7 +173,8 @@ extern "C" int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32
 // optional stage timing
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kStages = 7;
+constexpr int kStages = 8;
+constexpr int kStageLayer = 7;  // the single-launch layer kernel (stage 0: its prologue)
 constexpr int kRing = 128;
 // All timer state is touched only with `mu` held: a forward holds it from its
 // first to its last event while timing is on (so forwards on several host
@@ -192,7 +193,9 @@ StageTimer g_timer;
 
 void timer_drain_one(int slot) {
     StageTimer& T = g_timer;
-    (void)hipEventSynchronize(T.ev[slot][kStages]);
+    int last = kStages;
+    while (last > 0 && !T.used[slot][last]) --last;
+    (void)hipEventSynchronize(T.ev[slot][last]);
     int prev = -1;
     for (int s = 0; s <= kStages; ++s) {
         if (!T.used[slot][s]) continue;
@@ -341,12 +344,45 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, size_t prepa
                            deterministic_finalize, workspace, y, stream);
 }
 
+// Path a checked forward of this shape takes: MOE_PATH_MULTI or MOE_PATH_SINGLE,
+// or -1 when the setting asks for the single launch and the shape has none.
+static std::atomic<int> g_path{MOE_PATH_AUTO};
+
+static int resolve_path(int E, int T, int K, int mode) {
+    const long long R = (long long)T * K;
+    const bool ok = R <= kLayerMaxR && layer_supported((int)R, E, pick_bm_index(R, E), mode);
+    const int want = g_path.load();
+    if (want == MOE_PATH_MULTI) return MOE_PATH_MULTI;
+    if (want == MOE_PATH_SINGLE) return ok ? MOE_PATH_SINGLE : -1;
+    return ok ? MOE_PATH_SINGLE : MOE_PATH_MULTI;
+}
+
+extern "C" int moe_set_forward_path(int32_t path) {
+    if (path != MOE_PATH_AUTO && path != MOE_PATH_MULTI && path != MOE_PATH_SINGLE)
+        return fail(MOE_ERR_INVALID, "path=%d is not a moe_path", path);
+    g_path.store(path);
+    return MOE_OK;
+}
+
+extern "C" int moe_forward_path(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
+    int rc = check_dims(d);
+    if (rc) return -rc;
+    rc = check_mode(d, T, K, mode);
+    if (rc) return -rc;
+    const int p = resolve_path(d->E, T, K, mode);
+    if (p < 0) return -fail(MOE_ERR_UNSUPPORTED, "no single-launch layer for this shape");
+    return p;
+}
+
 // The launch sequence of one forward; every argument has been checked and
 // `workspace` holds at least forward_workspace_bytes(d, T, K, mode) bytes.
 int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
                          const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
                          int32_t router_weight_on_input, int32_t deterministic_finalize,
                          void* workspace, uint16_t* y, hipStream_t stream) {
+    const int path = resolve_path(d->E, T, K, mode);
+    if (path < 0) return fail(MOE_ERR_UNSUPPORTED, "no single-launch layer for this shape");
+    const bool single = path == MOE_PATH_SINGLE;
     WsPlan P;
     plan_workspace(*d, T, K, mode, &P);
 
@@ -371,14 +407,120 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     const bool f8 = mode == MOE_MXFP8;
     const bool per_row = mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6 || mx4;
     const int qkind = mode == MOE_W4A4_TOKEN_4O6 ? QK_NV_ROW_4O6 : (per_row ? QK_NV_ROW : QK_NV_TENSOR);
-    const bool fused = deterministic_finalize == 0;
+    const bool fused = deterministic_finalize == 0 && !single;
     uint32_t* status = reinterpret_cast<uint32_t*>(ws);
+
+    const int bmi = pick_bm_index(R, E);
+    const int BM = bm_of(bmi);
+    const int mt_max = (R + BM - 1) / BM + E;
+    const int32_t* tl = tiles + (size_t)bmi * (E + 1);
+    const int ab = mx4 ? AB_FP4 : (nv4 ? AB_F16_NV : (f8 ? AB_FP8 : AB_BF16_NV));
+
+    GemmArgs g1;
+    memset(&g1, 0, sizeof g1);
+    g1.a = mx4 ? (const void*)WS(uint8_t, V_XMXCODES)
+               : (nv4 ? (const void*)WS(uint16_t, V_XDEQ) : (f8 ? (const void*)WS(uint8_t, V_XCODES) : (const void*)x));
+    g1.a_scales = mx4 ? WS(uint8_t, V_XMXSCALES) : (f8 ? WS(uint8_t, V_XSCALES) : nullptr);
+    g1.a_g = nv4 ? WS(float, V_XG) : nullptr;
+    // the single launch stores a per-tensor scale at every row
+    g1.a_g_per_row = per_row || (single && nv4);
+    g1.gather = 1;
+    g1.row_to_route = r2r;
+    g1.topk = K;
+    g1.b_codes = blob + L.h.off_w1;
+    g1.b_scales = blob + L.h.off_s1;
+    g1.b_g = f8 ? nullptr : reinterpret_cast<const float*>(blob + L.h.off_g1);
+    g1.N = N1;
+    g1.Kdim = H;
+    g1.offsets = offsets;
+    g1.tiles = tl;
+    g1.E = E;
+    g1.mt_max = mt_max;
+    g1.act = act;
+    g1.on_input = router_weight_on_input;
+    g1.I = I;
+    g1.topw = topw;
+    if (nv4) {
+        g1.out_f32 = WS(float, V_A2F);
+    } else if (f8) {
+        g1.a2_codes = WS(uint8_t, V_A2CODES);
+        g1.a2_scales = WS(uint8_t, V_A2SCALES);
+    } else {
+        g1.out_bf16 = WS(uint16_t, V_A2F);
+    }
+    g1.amax_slot = mode == MOE_W4A4_TENSOR ? misc + kMiscA2Amax : nullptr;
+    g1.status = status;
+
+    GemmArgs g2;
+    memset(&g2, 0, sizeof g2);
+    g2.a = mx4 ? (const void*)WS(uint8_t, V_A2MXCODES)
+               : (nv4 ? (const void*)WS(uint16_t, V_A2DEQ)
+                      : (f8 ? (const void*)WS(uint8_t, V_A2CODES) : (const void*)WS(uint16_t, V_A2F)));
+    g2.a_scales = mx4 ? WS(uint8_t, V_A2MXSCALES) : (f8 ? WS(uint8_t, V_A2SCALES) : nullptr);
+    g2.a_g = nv4 ? WS(float, V_A2G) : nullptr;
+    g2.a_g_per_row = per_row || (single && nv4);
+    g2.gather = 0;
+    g2.row_to_route = r2r;
+    g2.topk = K;
+    g2.b_codes = blob + L.h.off_w2;
+    g2.b_scales = blob + L.h.off_s2;
+    g2.b_g = f8 ? nullptr : reinterpret_cast<const float*>(blob + L.h.off_g2);
+    g2.N = H;
+    g2.Kdim = I;
+    g2.offsets = offsets;
+    g2.tiles = tl;
+    g2.E = E;
+    g2.mt_max = mt_max;
+    g2.act = act;
+    g2.on_input = router_weight_on_input;
+    g2.I = I;
+    g2.topw = topw;
+    g2.out_f32 = WS(float, V_O);
+    g2.yacc = WS(float, V_YACC);
+    g2.fused = fused;
+    // a token accumulator well above the 256 MB last-level cache: N-block-major
+    // FC2 order, so each phase's atomics stay in cache
+    g2.phased = fused && (size_t)T * H * 4 > kPhasedYaccBytes;
+    g2.status = status;
 
     // while stage timing is on, the timer state belongs to this forward
     std::unique_lock<std::mutex> timing_lock(g_timer.mu, std::defer_lock);
     if (g_timer.enabled.load()) timing_lock.lock();
     const int tslot = timing_lock.owns_lock() && g_timer.enabled.load() ? timer_begin() : -1;
+    hipEvent_t t0, t1;
     timer_mark(tslot, 0, stream);
+
+    if (single) {
+        LayerArgs la;
+        memset(&la, 0, sizeof la);
+        la.g1 = g1;
+        la.g2 = g2;
+        la.logits = logits;
+        la.x = x;
+        la.T = T; la.H = H; la.I = I; la.E = E; la.K = K;
+        la.ids = ids; la.topw = topw; la.counts = counts; la.offsets = offsets; la.tiles = tiles;
+        la.r2r = r2r; la.rt2row = rt2row;
+        la.bmi = bmi;
+        la.xq = f8 ? LX_MX8
+                   : (!nv4 ? LX_NONE
+                           : (mode == MOE_W4A4_TOKEN_4O6 ? LX_NV_ROW_4O6 : (per_row ? LX_NV_ROW : LX_NV_TENSOR)));
+        la.xcodes = WS(uint8_t, V_XCODES); la.xscales = WS(uint8_t, V_XSCALES);
+        la.xg = WS(float, V_XG); la.xdeq = WS(uint16_t, V_XDEQ);
+        la.a2f = WS(float, V_A2F); la.a2codes = WS(uint8_t, V_A2CODES); la.a2scales = WS(uint8_t, V_A2SCALES);
+        la.a2g = WS(float, V_A2G); la.a2deq = WS(uint16_t, V_A2DEQ);
+        la.misc = misc;
+        la.y = y;
+        la.sync = WS(uint32_t, V_SYNC);
+        la.mt_max = layer_mt_bound(R, E);
+        la.status = status;
+        timer_kernel_events(tslot, kStageLayer, &t0, &t1);
+        HIP_TRY(launch_layer(la, ab, blob, L.h, layer_sync_words(T, H, la.mt_max), stream, t0, t1),
+                "single-launch layer");
+#undef WS
+        return MOE_OK;
+    }
+#define WS(T_, v) reinterpret_cast<T_*>(ws + P.off[v])
+
     HIP_TRY(launch_route(logits, T, E, K, ids, topw, misc, blob, L.h, status, stream), "route");
     timer_mark(tslot, 1, stream);
     if (small_route_permute(R, E)) {
@@ -407,46 +549,6 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
                 "quantize x");
     }
 
-    const int bmi = pick_bm_index(R, E);
-    const int BM = bm_of(bmi);
-    const int mt_max = (R + BM - 1) / BM + E;
-    const int32_t* tl = tiles + (size_t)bmi * (E + 1);
-    const int ab = mx4 ? AB_FP4 : (nv4 ? AB_F16_NV : (f8 ? AB_FP8 : AB_BF16_NV));
-
-    GemmArgs g1;
-    memset(&g1, 0, sizeof g1);
-    g1.a = mx4 ? (const void*)WS(uint8_t, V_XMXCODES)
-               : (nv4 ? (const void*)WS(uint16_t, V_XDEQ) : (f8 ? (const void*)WS(uint8_t, V_XCODES) : (const void*)x));
-    g1.a_scales = mx4 ? WS(uint8_t, V_XMXSCALES) : (f8 ? WS(uint8_t, V_XSCALES) : nullptr);
-    g1.a_g = nv4 ? WS(float, V_XG) : nullptr;
-    g1.a_g_per_row = per_row;
-    g1.gather = 1;
-    g1.row_to_route = r2r;
-    g1.topk = K;
-    g1.b_codes = blob + L.h.off_w1;
-    g1.b_scales = blob + L.h.off_s1;
-    g1.b_g = f8 ? nullptr : reinterpret_cast<const float*>(blob + L.h.off_g1);
-    g1.N = N1;
-    g1.Kdim = H;
-    g1.offsets = offsets;
-    g1.tiles = tl;
-    g1.E = E;
-    g1.mt_max = mt_max;
-    g1.act = act;
-    g1.on_input = router_weight_on_input;
-    g1.I = I;
-    g1.topw = topw;
-    if (nv4) {
-        g1.out_f32 = WS(float, V_A2F);
-    } else if (f8) {
-        g1.a2_codes = WS(uint8_t, V_A2CODES);
-        g1.a2_scales = WS(uint8_t, V_A2SCALES);
-    } else {
-        g1.out_bf16 = WS(uint16_t, V_A2F);
-    }
-    g1.amax_slot = mode == MOE_W4A4_TENSOR ? misc + kMiscA2Amax : nullptr;
-    g1.status = status;
-    hipEvent_t t0, t1;
     timer_kernel_events(tslot, 3, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC1, bmi, g1, stream, t0, t1), "FC1");
 
@@ -462,37 +564,6 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     }
 
     if (fused) HIP_TRY(launch_fill_u32(WS(uint32_t, V_YACC), (size_t)T * H, 0u, stream), "zero y_acc");
-    GemmArgs g2;
-    memset(&g2, 0, sizeof g2);
-    g2.a = mx4 ? (const void*)WS(uint8_t, V_A2MXCODES)
-               : (nv4 ? (const void*)WS(uint16_t, V_A2DEQ)
-                      : (f8 ? (const void*)WS(uint8_t, V_A2CODES) : (const void*)WS(uint16_t, V_A2F)));
-    g2.a_scales = mx4 ? WS(uint8_t, V_A2MXSCALES) : (f8 ? WS(uint8_t, V_A2SCALES) : nullptr);
-    g2.a_g = nv4 ? WS(float, V_A2G) : nullptr;
-    g2.a_g_per_row = per_row;
-    g2.gather = 0;
-    g2.row_to_route = r2r;
-    g2.topk = K;
-    g2.b_codes = blob + L.h.off_w2;
-    g2.b_scales = blob + L.h.off_s2;
-    g2.b_g = f8 ? nullptr : reinterpret_cast<const float*>(blob + L.h.off_g2);
-    g2.N = H;
-    g2.Kdim = I;
-    g2.offsets = offsets;
-    g2.tiles = tl;
-    g2.E = E;
-    g2.mt_max = mt_max;
-    g2.act = act;
-    g2.on_input = router_weight_on_input;
-    g2.I = I;
-    g2.topw = topw;
-    g2.out_f32 = WS(float, V_O);
-    g2.yacc = WS(float, V_YACC);
-    g2.fused = fused;
-    // a token accumulator well above the 256 MB last-level cache: N-block-major
-    // FC2 order, so each phase's atomics stay in cache
-    g2.phased = fused && (size_t)T * H * 4 > kPhasedYaccBytes;
-    g2.status = status;
     timer_kernel_events(tslot, 5, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream, t0, t1), "FC2");
 
