@@ -24,9 +24,7 @@ VIEWS = {"topk_ids": 0, "topk_w": 1, "counts": 2, "offsets": 3, "row_to_route": 
          "route_to_row": 5, "x_codes": 6, "x_scales": 7, "x_g": 8, "a2_pre": 9,
          "a2_codes": 10, "a2_scales": 11, "a2_g": 12, "o": 13, "x_mx_codes": 14,
          "x_mx_scales": 15, "a2_mx_codes": 16, "a2_mx_scales": 17}
-STAGES = ["route", "permute", "quantize_x", "fc1", "quantize_fc2_input", "fc2", "finalize",
-          "layer"]
-PATHS = {"auto": 0, "multi": 1, "single": 2}
+STAGES = ["route", "permute", "quantize_x", "fc1", "quantize_fc2_input", "fc2", "finalize"]
 
 
 class MoeError(RuntimeError):
@@ -60,8 +58,6 @@ def _load():
         "moe_quantize": (ctypes.c_int, [P, i32, i32, i32, P, P, P, P, P]),
         "moe_workspace_view": (ctypes.c_int, [D, i32, i32, i32, i32, ctypes.POINTER(sz),
                                               ctypes.POINTER(sz)]),
-        "moe_set_forward_path": (ctypes.c_int, [i32]),
-        "moe_forward_path": (ctypes.c_int, [D, i32, i32, i32]),
         "moe_stage_timing": (ctypes.c_int, [i32]),
         "moe_stage_times": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float), i32,
                                            ctypes.POINTER(i32)]),
@@ -76,7 +72,7 @@ def _load():
 _lib = _load()
 EXPORTS = ["moe_prepared_bytes", "moe_prepare_weights", "moe_check_prepared",
            "moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_forward_status",
-           "moe_finalize", "moe_quantize", "moe_set_forward_path", "moe_forward_path",
+           "moe_finalize", "moe_quantize",
            "moe_workspace_view", "moe_stage_timing", "moe_stage_times", "moe_last_error"]
 
 
@@ -287,21 +283,6 @@ def workspace_view(d: Dims, workspace: torch.Tensor, T: int, K: int, mode: str, 
     else:
         dt = _VIEW_DTYPES[vid]
     return raw.view(dt)
-
-
-def set_forward_path(path: str):
-    """Process-wide forward path: "auto" (the single-launch layer where it
-    applies), "multi" (one launch per stage) or "single" (shapes without a
-    single-launch layer then fail)."""
-    _check(_lib.moe_set_forward_path(PATHS[path]))
-
-
-def forward_path(d: Dims, T: int, K: int, mode: str) -> str:
-    """The path ("multi" or "single") a forward of this shape takes now."""
-    rc = _lib.moe_forward_path(ctypes.byref(d.c()), T, K, MODES[mode])
-    if rc < 0:
-        raise MoeError(-rc, _lib.moe_last_error().decode())
-    return {1: "multi", 2: "single"}[rc]
 
 
 def stage_timing(enable: bool):

@@ -173,8 +173,7 @@ extern "C" int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32
 // optional stage timing
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kStages = 8;
-constexpr int kStageLayer = 7;  // the single-launch layer kernel (stage 0: its prologue)
+constexpr int kStages = 7;
 constexpr int kRing = 128;
 // All timer state is touched only with `mu` held: a forward holds it from its
 // first to its last event while timing is on (so forwards on several host
@@ -344,45 +343,12 @@ extern "C" int moe_forward(const moe_dims* d, const void* prepared, size_t prepa
                            deterministic_finalize, workspace, y, stream);
 }
 
-// Path a checked forward of this shape takes: MOE_PATH_MULTI or MOE_PATH_SINGLE,
-// or -1 when the setting asks for the single launch and the shape has none.
-static std::atomic<int> g_path{MOE_PATH_AUTO};
-
-static int resolve_path(int E, int T, int K, int mode) {
-    const long long R = (long long)T * K;
-    const bool ok = R <= kLayerMaxR && layer_supported((int)R, E, pick_bm_index(R, E), mode);
-    const int want = g_path.load();
-    if (want == MOE_PATH_MULTI) return MOE_PATH_MULTI;
-    if (want == MOE_PATH_SINGLE) return ok ? MOE_PATH_SINGLE : -1;
-    return ok ? MOE_PATH_SINGLE : MOE_PATH_MULTI;
-}
-
-extern "C" int moe_set_forward_path(int32_t path) {
-    if (path != MOE_PATH_AUTO && path != MOE_PATH_MULTI && path != MOE_PATH_SINGLE)
-        return fail(MOE_ERR_INVALID, "path=%d is not a moe_path", path);
-    g_path.store(path);
-    return MOE_OK;
-}
-
-extern "C" int moe_forward_path(const moe_dims* d, int32_t T, int32_t K, int32_t mode) {
-    int rc = check_dims(d);
-    if (rc) return -rc;
-    rc = check_mode(d, T, K, mode);
-    if (rc) return -rc;
-    const int p = resolve_path(d->E, T, K, mode);
-    if (p < 0) return -fail(MOE_ERR_UNSUPPORTED, "no single-launch layer for this shape");
-    return p;
-}
-
 // The launch sequence of one forward; every argument has been checked and
 // `workspace` holds at least forward_workspace_bytes(d, T, K, mode) bytes.
 int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t* x,
                          const float* logits, int32_t T, int32_t K, int32_t mode, int32_t act,
                          int32_t router_weight_on_input, int32_t deterministic_finalize,
                          void* workspace, uint16_t* y, hipStream_t stream) {
-    const int path = resolve_path(d->E, T, K, mode);
-    if (path < 0) return fail(MOE_ERR_UNSUPPORTED, "no single-launch layer for this shape");
-    const bool single = path == MOE_PATH_SINGLE;
     WsPlan P;
     plan_workspace(*d, T, K, mode, &P);
 
@@ -407,7 +373,7 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     const bool f8 = mode == MOE_MXFP8;
     const bool per_row = mode == MOE_W4A4_TOKEN || mode == MOE_W4A4_TOKEN_4O6 || mx4;
     const int qkind = mode == MOE_W4A4_TOKEN_4O6 ? QK_NV_ROW_4O6 : (per_row ? QK_NV_ROW : QK_NV_TENSOR);
-    const bool fused = deterministic_finalize == 0 && !single;
+    const bool fused = deterministic_finalize == 0;
     uint32_t* status = reinterpret_cast<uint32_t*>(ws);
 
     const int bmi = pick_bm_index(R, E);
@@ -422,8 +388,7 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
                : (nv4 ? (const void*)WS(uint16_t, V_XDEQ) : (f8 ? (const void*)WS(uint8_t, V_XCODES) : (const void*)x));
     g1.a_scales = mx4 ? WS(uint8_t, V_XMXSCALES) : (f8 ? WS(uint8_t, V_XSCALES) : nullptr);
     g1.a_g = nv4 ? WS(float, V_XG) : nullptr;
-    // the single launch stores a per-tensor scale at every row
-    g1.a_g_per_row = per_row || (single && nv4);
+    g1.a_g_per_row = per_row;
     g1.gather = 1;
     g1.row_to_route = r2r;
     g1.topk = K;
@@ -458,7 +423,7 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
                       : (f8 ? (const void*)WS(uint8_t, V_A2CODES) : (const void*)WS(uint16_t, V_A2F)));
     g2.a_scales = mx4 ? WS(uint8_t, V_A2MXSCALES) : (f8 ? WS(uint8_t, V_A2SCALES) : nullptr);
     g2.a_g = nv4 ? WS(float, V_A2G) : nullptr;
-    g2.a_g_per_row = per_row || (single && nv4);
+    g2.a_g_per_row = per_row;
     g2.gather = 0;
     g2.row_to_route = r2r;
     g2.topk = K;
@@ -489,37 +454,6 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     const int tslot = timing_lock.owns_lock() && g_timer.enabled.load() ? timer_begin() : -1;
     hipEvent_t t0, t1;
     timer_mark(tslot, 0, stream);
-
-    if (single) {
-        LayerArgs la;
-        memset(&la, 0, sizeof la);
-        la.g1 = g1;
-        la.g2 = g2;
-        la.logits = logits;
-        la.x = x;
-        la.T = T; la.H = H; la.I = I; la.E = E; la.K = K;
-        la.ids = ids; la.topw = topw; la.counts = counts; la.offsets = offsets; la.tiles = tiles;
-        la.r2r = r2r; la.rt2row = rt2row;
-        la.bmi = bmi;
-        la.xq = f8 ? LX_MX8
-                   : (!nv4 ? LX_NONE
-                           : (mode == MOE_W4A4_TOKEN_4O6 ? LX_NV_ROW_4O6 : (per_row ? LX_NV_ROW : LX_NV_TENSOR)));
-        la.xcodes = WS(uint8_t, V_XCODES); la.xscales = WS(uint8_t, V_XSCALES);
-        la.xg = WS(float, V_XG); la.xdeq = WS(uint16_t, V_XDEQ);
-        la.a2f = WS(float, V_A2F); la.a2codes = WS(uint8_t, V_A2CODES); la.a2scales = WS(uint8_t, V_A2SCALES);
-        la.a2g = WS(float, V_A2G); la.a2deq = WS(uint16_t, V_A2DEQ);
-        la.misc = misc;
-        la.y = y;
-        la.sync = WS(uint32_t, V_SYNC);
-        la.mt_max = layer_mt_bound(R, E);
-        la.status = status;
-        timer_kernel_events(tslot, kStageLayer, &t0, &t1);
-        HIP_TRY(launch_layer(la, ab, blob, L.h, layer_sync_words(T, H, la.mt_max), stream, t0, t1),
-                "single-launch layer");
-#undef WS
-        return MOE_OK;
-    }
-#define WS(T_, v) reinterpret_cast<T_*>(ws + P.off[v])
 
     HIP_TRY(launch_route(logits, T, E, K, ids, topw, misc, blob, L.h, status, stream), "route");
     timer_mark(tslot, 1, stream);

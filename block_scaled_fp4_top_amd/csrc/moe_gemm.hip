@@ -1,21 +1,250 @@
-// S4/S6 grouped GEMMs: the standalone kernels (one launch per GEMM) and their
-// host launchers. The tile itself (K loop, operand formats, epilogues) is in
-// moe_gemm_tile.h.
+// S4/S6 grouped GEMMs with fused epilogues.
+//
+// C[r][n] = sum_k A[row(r)][k] * W_e[n][k] for the rows r of one expert e.
+// A block of NW waves (4, or 8 for wide tiles) owns an M-tile of BM rows of
+// one expert (from the device tile list built by the permutation) and NW*WN
+// strips of 16 output columns; wave w owns strips [w*WN, w*WN + WN) and all
+// rows of the tile.
+//  - A (activations) is staged through LDS per 128-deep K step by direct
+//    global->LDS loads: f16/bf16 as 8 rows x one 128-byte line per load, in an
+//    XOR-swizzled layout whose operand reads are free of bank conflicts; fp8
+//    in the operand's own order (16 rows x 64 bytes per load).
+//  - B (weights) is read straight from HBM into registers: the prepared blob
+//    stores every 16 x 128 micro-tile as the register image of a 64-lane wave,
+//    so each load is a contiguous 1 KB (NVFP4) or 2 KB (MXFP8) per wave.
+//  - P-stage software pipeline: the loads of the next P-1 steps are in flight
+//    while one step is multiplied (P LDS buffers for A, P register sets for B).
+//  - Small tiles (decode): one contiguous range of tiles per XCD, and, when
+//    every block is resident at once, wave priorities that let the blocks
+//    furthest behind in their K loop issue first.
+//  - NVFP4: exact dequantization code * sf in registers (hardware fp4
+//    converter at unit scale, then the E4M3 block scale: a packed fp16 multiply
+//    for fp16 operands, an fp32 multiply for bf16; the product has at most 6
+//    significant bits, so it is exact), then v_mfma_f32_16x16x32_{f16,bf16}.
+//    The E4M3 block-16 scales do not fit the matrix cores' E8M0 block-32
+//    scaling, so the scale is applied on the VALU.
+//  - MXFP8: v_mfma_scale_f32_16x16x128_f8f6f4 with the E8M0 block scales as
+//    the per-lane scale operands; no dequantization at all.
+//  - Epilogue: global scales (g_a * g_w), then FC1: SwiGLU/ReLU2, optional
+//    input-side router weight in FP32, then the FC2 input: fp32 (+ partial
+//    maxima of |value| for the per-tensor global scale) for
+//    NVFP4, bf16 for W4A16, or MXFP8 codes and scales quantized in place;
+//    FC2: store of the permuted output or fp32 atomic scatter-add into the
+//    token accumulator (fused finalize).
 #include <hip/hip_ext.h>
 
 #include <atomic>
+#include <type_traits>
 
-#include "moe_gemm_tile.h"
+#include "moe_internal.h"
+#include "moe_kernels.h"
 
 namespace moe {
 
-// Standalone grouped-GEMM kernel: block blockIdx.x -> (M-tile, N-block) in an
-// XCD-aware order, then one tile.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_pair(float lo, float hi, bool bf16) {
+    if (bf16) return __builtin_amdgcn_perm(f2u(hi), f2u(lo), 0x07060302u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// SiLU(g) * u with the hardware exp2 and reciprocal (a few ulp in fp32).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 1.44269504f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// Epilogue: acc[ms][s][i] holds C for row ms*16 + 4*(lane/16) + i of the
+// tile and column strip gs0 + s, lane % 16.
+// Max over the 16 lanes of each DPP row (lanes with equal lane/16), by
+// rotations within the row: every lane ends with the row's max.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+    return v;
+}
+
+template <int AB, int MS, int WN, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS][WN], int e,
+                                              int row0, int rows, const int* s_arow, int gs0,
+                                              int lane) {
+    const float gw = p.b_g ? p.b_g[e] : 1.0f;
+    const int c16 = lane & 15;
+    if constexpr (EPI == EPI_FC1 && AB == AB_FP8) {
+        // MXFP8: the wave holds 32 consecutive FC2-input columns of each row
+        // per pair of output strips (lanes with equal lane/16 share a row), so
+        // it quantizes whole 32-element blocks: block max over the 16 lanes of
+        // the row group, E8M0 exponent, E4M3 codes. All lanes compute (rows
+        // past the group hold finite values of a re-read row); stores are
+        // guarded.
+        constexpr int OS = WN / 2;  // SwiGLU output strips; ReLU2 has WN
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = ms * 16 + 4 * (lane >> 4) + i;
+                const int row = row0 + min(m, rows - 1);
+                const float pw = p.on_input ? p.topw[p.row_to_route[row]] : 1.0f;
+                float a[WN];
+                int nout;
+                if (p.act == MOE_ACT_SWIGLU) {
+                    nout = OS;
+#pragma unroll
+                    for (int u = 0; u < OS; ++u) {
+                        a[u] = silu_mul(acc[ms][2 * u][i] * gw, acc[ms][2 * u + 1][i] * gw);
+                        if (p.on_input) a[u] = a[u] * pw;
+                    }
+                } else {
+                    nout = WN;
+#pragma unroll
+                    for (int u = 0; u < WN; ++u) {
+                        const float h = acc[ms][u][i] * gw;
+                        a[u] = h > 0.0f ? h * h : 0.0f;
+                        if (p.on_input) a[u] = a[u] * pw;
+                    }
+                }
+                const int col0 = (p.act == MOE_ACT_SWIGLU ? gs0 >> 1 : gs0) * 16;
+#pragma unroll
+                for (int b = 0; b < WN / 2; ++b) {
+                    if (2 * b + 1 >= nout) break;  // the host launches whole blocks only
+                    float ab = fmaxf(fabsf(a[2 * b]), fabsf(a[2 * b + 1]));
+                    ab = row16_max(ab);
+                    const int X = mxfp8_exponent(ab);
+                    const float inv = mxfp8_inv_scale(X);
+                    if (m < rows) {
+                        const size_t o = (size_t)(row0 + m) * p.I + col0 + 32 * b + c16;
+                        const uint32_t c = e4m3_code2(__fmul_rn(a[2 * b], inv), __fmul_rn(a[2 * b + 1], inv));
+                        p.a2_codes[o] = (uint8_t)c;
+                        p.a2_codes[o + 16] = (uint8_t)(c >> 8);
+                        if (c16 == 0)
+                            p.a2_scales[(size_t)(row0 + m) * (p.I / 32) + (col0 >> 5) + b] = (uint8_t)(X + 127);
+                    }
+                }
+            }
+        }
+    } else {
+    float amax = 0.0f;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = ms * 16 + 4 * (lane >> 4) + i;
+            if (m >= rows) continue;
+            const int row = row0 + m;
+            const float ga = p.a_g ? p.a_g[p.a_g_per_row ? s_arow[m] : 0] : 1.0f;
+            const float sc = ga * gw;
+            if (EPI == EPI_FC1) {
+                const float pw = p.on_input ? p.topw[p.row_to_route[row]] : 1.0f;
+                if (p.act == MOE_ACT_SWIGLU) {
+#pragma unroll
+                    for (int u = 0; u < WN / 2; ++u) {
+                        float a = silu_mul(acc[ms][2 * u][i] * sc, acc[ms][2 * u + 1][i] * sc);
+                        if (p.on_input) a = a * pw;
+                        const int col = ((gs0 + 2 * u) >> 1) * 16 + c16;
+                        if (p.out_bf16) p.out_bf16[(size_t)row * p.I + col] = bf16_rne(a);
+                        else p.out_f32[(size_t)row * p.I + col] = a;
+                        amax = fmaxf(amax, fabsf(a));
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const float h = acc[ms][s][i] * sc;
+                        float a = h > 0.0f ? h * h : 0.0f;
+                        if (p.on_input) a = a * pw;
+                        const int col = (gs0 + s) * 16 + c16;
+                        if (p.out_bf16) p.out_bf16[(size_t)row * p.I + col] = bf16_rne(a);
+                        else p.out_f32[(size_t)row * p.I + col] = a;
+                        amax = fmaxf(amax, fabsf(a));
+                    }
+                }
+            } else {
+                if (p.fused) {
+                    const int route = p.row_to_route[row];
+                    const int t = route / p.topk;
+                    const float w = p.on_input ? 1.0f : p.topw[route];
+#pragma unroll
+                    for (int s = 0; s < WN; ++s)
+                        atomicAdd(&p.yacc[(size_t)t * p.N + (gs0 + s) * 16 + c16], w * (acc[ms][s][i] * sc));
+                } else {
+#pragma unroll
+                    for (int s = 0; s < WN; ++s)
+                        p.out_f32[(size_t)row * p.N + (gs0 + s) * 16 + c16] = acc[ms][s][i] * sc;
+                }
+            }
+        }
+    }
+    if (EPI == EPI_FC1 && p.amax_slot) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+        const int slot = (blockIdx.x * 4 + (threadIdx.x >> 6)) % kAmaxSlots;
+        if (lane == 0) atomicMax(p.amax_slot + slot * kAmaxStride, f2u(amax));
+    }
+    }
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base is uniform across the wave).
+__device__ __forceinline__ void lds_load16(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)gsrc,
+        (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* gsrc, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)gsrc,
+        (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+}
+
+// s_waitcnt until at most N vector-memory operations of this wave are
+// outstanding and all LDS operations are done (export counter not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Orders the first use of a loaded register after the preceding wait: the
+// empty volatile asm "redefines" the value, so no instruction reading it can
+// be scheduled above the asm (and volatile asm keeps its order).
+__device__ __forceinline__ void reg_fence(uint32_t& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void reg_fence(u32x4& v) { asm volatile("" : "+v"(v)); }
+
+// Workgroup barrier without the fence __syncthreads() carries (that fence
+// drains every outstanding load, which would serialise the pipeline). The
+// caller waits for the loads that must have landed; the memory clobber keeps
+// the compiler from moving memory accesses across.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Grouped GEMM tile kernel. P-stage software pipeline over 128-deep K steps:
+// while step kt is multiplied, the loads of steps kt+1 .. kt+P-1 are in
+// flight (A into P rotating LDS buffers by direct loads, B into P rotating
+// register sets). Every wave issues the same number L of loads per step
+// (padding loads target a scratch LDS area), so "step kt has landed" is the
+// wait vmcnt <= L*(P-2) followed by a barrier.
 template <int AB, int BM, int WN, int EPI, int P, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
-    __shared__ GemmSmem<AB, BM, P> sm;
-    const int lane = threadIdx.x & 63;
-    const int vb = blockIdx.x, nvb = gridDim.x;
+    constexpr bool F8 = AB == AB_FP8;
+    constexpr bool F4 = AB == AB_FP4;
+    constexpr bool SC = F8 || F4;  // block-scaled matrix core (E8M0 scale per 32)
+    constexpr int A_ROW = F8 ? 128 : (F4 ? 64 : 256);  // bytes of one A row per K step
+    constexpr int A_TILE = BM * A_ROW;
+    __shared__ __attribute__((aligned(1024))) uint8_t sA[P][A_TILE];
+    // A scales (fp8, fp4): one wave-wide 4-byte direct load per step writes 64
+    // words, so each buffer holds at least 64 rows' words even for BM < 64.
+    __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][SC ? (BM > 64 ? BM : 64) : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
+    __shared__ int s_arow[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
     // the forward's status word, loaded here and tested after the tile lookup
     // so that its latency overlaps the lookup's loads
     const uint32_t status = p.status ? *p.status : 0u;
@@ -43,8 +272,8 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         const int NB = p.N / (16 * NW * WN);
         const int work = p.tiles[p.E] * NB;  // <= the grid: tiles[E] <= mt_max
         const int per = (work + 7) >> 3;
-        const int j = vb >> 3;
-        const int w = (vb & 7) * per + j;
+        const int j = blockIdx.x >> 3;
+        const int w = (blockIdx.x & 7) * per + j;
         if (j >= per || w >= work) return;
         mt = w / NB;
         nb = w % NB;
@@ -54,19 +283,313 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         const int act = p.tiles[p.E];
         const int per = (act + 7) >> 3;
         if (per == 0) return;  // no rows (a forward always has some)
-        const int j = vb >> 3;
+        const int j = blockIdx.x >> 3;
         nb = j / per;
-        mt = (vb & 7) * per + j % per;
+        mt = (blockIdx.x & 7) * per + j % per;
         if (nb >= NB || mt >= act) return;
     } else {
-        const int id = (vb & 7) * (nvb >> 3) + (vb >> 3);
+        const int id = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
         mt = id % p.mt_max;
         nb = id / p.mt_max;
         if (nb >= p.N / (16 * NW * WN) || mt >= p.tiles[p.E]) return;
     }
-    const TileLoc loc = tile_locate<BM>(p, mt, lane);
+    // Expert of M-tile mt: the last e with tiles[e] <= mt (tiles[] is the
+    // exclusive prefix of the experts' tile counts, so empty experts repeat
+    // their successor's entry and are skipped).
+    int e;
+    if constexpr (BM <= 32) {
+        // one wave-wide load and ballot per 64 experts instead of a chain of
+        // dependent loads: these blocks are all resident at once, so their
+        // start-up latency is on the kernel's critical path
+        int cnt = 0;
+        for (int base = 0; base < p.E; base += 64) {
+            const int ee = base + lane;
+            cnt += __popcll(__ballot(ee < p.E && p.tiles[ee] <= mt));
+        }
+        e = cnt - 1;
+    } else {
+        int lo = 0, hi = p.E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+        }
+        e = lo;
+    }
+    const int mt_local = mt - p.tiles[e];
+    const int row0 = p.offsets[e] + mt_local * BM;
+    const int rows = min(BM, p.offsets[e + 1] - row0);
     if (status) return;  // blob prepared for other dimensions: no weight reads, no stores
-    gemm_tile_run<AB, BM, WN, EPI, P, NW>(p, sm, loc, nb, fair, threadIdx.x);
+    for (int m = tid; m < BM; m += NW * 64)
+        s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
+    __syncthreads();
+
+    // Main loop and epilogue of one tile whose rows fit in MS 16-row groups
+    // (MS <= the kernel's BM / 16): the launch picks the smallest MS that covers
+    // the tile, so an expert's last, partly filled tile runs fewer matrix-core
+    // operations and loads.
+    auto body = [&](auto ms_tag) {
+        constexpr int MS = decltype(ms_tag)::value;
+        constexpr bool BF = AB == AB_BF16_NV;
+        const int KT = p.Kdim / kTileK;
+        const size_t tiles_e = (size_t)(p.N / kStrip) * KT;
+        const int gs0 = nb * (NW * WN) + wave * WN;  // first global strip of this wave
+        const uint8_t* abase = static_cast<const uint8_t*>(p.a);
+        const size_t a_row_bytes = F4 ? (size_t)p.Kdim / 2 : (size_t)p.Kdim * (F8 ? 1 : 2);
+        const int r_any = s_arow[0];                 // rows past the group re-read a valid row
+
+        // A staging: every 1 KB of the LDS tile is one wave-wide direct load
+        // (lane l lands at byte 16 l).
+        //  f16/bf16: block blk = 4 ms + 2 h + g holds rows ms*16 + 8 g + [0, 8),
+        //    bytes 128 h + [0, 128) of the 256-byte K step: each row's request is
+        //    one full 128-byte line. Row r (0..15 in its group) puts its 16-byte
+        //    chunk c at slot (r % 8) * 8 + (c ^ (r % 8) ^ 7 (r / 8)): the 64
+        //    addresses of one matrix-core operand read (16 rows, one chunk each)
+        //    then differ modulo 1 KB and, within every 8-lane group, modulo 128
+        //    bytes, which keeps the read free of bank conflicts (checked with the
+        //    LDS conflict counter; without the factor 7 the reads conflicted).
+        //  fp8: block blk = 2 ms + h holds lane l' = row ms*16 + l'%16,
+        //    k = 64 h + 16 (l'/16) + [0, 16), the operand's own order (the
+        //    128-byte-row form measured 3 % slower here).
+        //  fp4: block blk = ms holds lane l' = row ms*16 + l'%16, packed
+        //    k = 32 (l'/16) + [0, 32) (bytes 16 (l'/16) + [0, 16) of the row's
+        //    64-byte step): the lane's 32 values are the one 32-block whose
+        //    E8M0 scale that lane supplies (probed on gfx950).
+        // Wave w loads the blocks w, w + NW, w + 2 NW, ...
+        constexpr int JB = F8 ? 2 : (F4 ? 1 : 4);
+        constexpr int AB_PER_WAVE = (MS * JB + NW - 1) / NW;
+        uint32_t aoff[AB_PER_WAVE];  // byte offset of the lane's A row chunk (A < 4 GiB)
+        int adst[AB_PER_WAVE];
+#pragma unroll
+        for (int i = 0; i < AB_PER_WAVE; ++i) {
+            const int blk = wave + NW * i;
+            const int ms = blk / JB, g = blk & 1, h = (blk % JB) >> 1;
+            const int r8 = lane >> 3;  // row within the 8-row half
+            const int koff = F4 ? 16 * (lane >> 4)
+                                : (F8 ? g * 64 + 16 * (lane >> 4) : h * 128 + (((lane & 7) ^ r8 ^ (7 * g)) << 4));
+            int r = r_any;
+            if (ms < MS) {
+                const int rr = s_arow[ms * 16 + (SC ? (lane & 15) : 8 * g + r8)];
+                r = rr >= 0 ? rr : r_any;
+            }
+            aoff[i] = (uint32_t)((size_t)r * a_row_bytes + koff);
+            adst[i] = (ms < MS) ? blk * 1024 : -1;   // -1: padding load into sJunk
+        }
+        const uint8_t* ascsrc = nullptr;
+        if (SC) {
+            const int m = wave * 64 + lane;
+            const int rr = m < MS * 16 ? s_arow[m] : -1;
+            ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
+        }
+        constexpr int L = AB_PER_WAVE + (SC ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
+
+        // Weight loads: small M tiles read each weight once, so they stream past
+    // the caches (non-temporal); wide tiles rely on L2 hits across the M-tiles
+    // of one expert and load normally.
+    auto load_b = [](const u32x4* q) -> u32x4 {
+        if constexpr (BM <= 32) return __builtin_nontemporal_load(q);
+        else return *q;
+    };
+    // one step's loads; ks >= KT issues the same number of loads as padding
+        auto issue = [&](int ks, int buf, u32x4* c1, u32x4* c2, uint32_t* sc) {
+            const bool real = ks < KT;
+            const int kk = real ? ks : KT - 1;
+#pragma unroll
+            for (int i = 0; i < AB_PER_WAVE; ++i)
+                lds_load16(abase + aoff[i] + (size_t)kk * A_ROW, (real && adst[i] >= 0) ? (void*)&sA[buf][adst[i]] : (void*)sJunk);
+            if (SC) lds_load4(ascsrc + kk * 4, (real && wave * 64 < MS * 16) ? (void*)&sAsc[buf][wave * 64] : (void*)sJunk);
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                const size_t tile = (size_t)e * tiles_e + (size_t)(gs0 + s) * KT + kk;
+                if (F8) {
+                    const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
+                    c1[s] = load_b(q);
+                    c2[s] = load_b(q + 1);
+                    sc[s] = p.b_scales[tile * kF8TileScale + lane];
+                } else if (F4) {
+                    c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kF4TileBytes + lane * 16));
+                    sc[s] = p.b_scales[tile * kF4TileScale + lane];
+                } else {
+                    c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16));
+                    sc[s] = *reinterpret_cast<const uint32_t*>(
+                        p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
+                }
+            }
+        };
+
+        f32x4 acc[MS][WN];
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+            for (int s = 0; s < WN; ++s) acc[ms][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // f16/bf16: this lane's operand chunk in the staged A tile: row lane % 16,
+        // chunk lane / 16 (+ 4 for the second 64 bytes of a 128-byte half).
+        const int a_r7 = lane & 7, a_g = (lane >> 3) & 1;
+        const int a_slot0 = a_g * 1024 + a_r7 * 128 + (((lane >> 4) ^ a_r7 ^ (7 * a_g)) << 4);
+        const int a_slot1 = a_slot0 ^ 64;
+        auto compute = [&](int buf, const u32x4* bc, const u32x4* bc2, const uint32_t* bs) {
+            if (F4) {
+                // E2M1 operands, four VGPRs each (the instruction reads no more
+                // for fp4), E8M0 scales of the lane's 32-block
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 1024 + lane * 16]);
+                    const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
+                    const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w, 0, 0, 0, 0};
+                        acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc[ms][s], 4, 4, 0, asc, 0, (int)bs[s]);
+                    }
+                }
+            } else if (F8) {
+#pragma unroll
+                for (int ms = 0; ms < MS; ++ms) {
+                    const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + lane * 16]);
+                    const uint4 a1 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 2048 + 1024 + lane * 16]);
+                    const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                      (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w,
+                                          (int)bc2[s].x, (int)bc2[s].y, (int)bc2[s].z, (int)bc2[s].w};
+                        acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, bv, acc[ms][s], 0, 0, 0, asc, 0, (int)bs[s]);
+                    }
+                }
+            } else if (!BF) {
+                // fp16 operands: each E2M1 pair converts to two fp16 values, then
+                // one packed multiply by the block scale (E4M3, exact in fp16);
+                // code * scale has at most 6 significant bits and lies in
+                // [2^-10, 2688], so the product is exact.
+                h2 sfp[WN][2];
+#pragma unroll
+                for (int s = 0; s < WN; ++s) {
+                    sfp[s][0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, false);
+                    sfp[s][1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bs[s], 1.0f, true);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    u32x4 bq[WN];
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const uint32_t w = bc[s][j];
+                        const h2 f = (j & 1) ? sfp[s][j >> 1].yy : sfp[s][j >> 1].xx;
+                        const h2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * f;
+                        const h2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * f;
+                        const h2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * f;
+                        const h2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * f;
+                        bq[s] = u32x4{__builtin_bit_cast(uint32_t, c0), __builtin_bit_cast(uint32_t, c1),
+                                      __builtin_bit_cast(uint32_t, c2), __builtin_bit_cast(uint32_t, c3)};
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            &sA[buf][(ms * 4 + (j >> 1) * 2) * 1024 + ((j & 1) ? a_slot1 : a_slot0)]);
+#pragma unroll
+                        for (int s = 0; s < WN; ++s)
+                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                                __builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, bq[s]), acc[ms][s], 0, 0, 0);
+                    }
+                    // keep each 32-deep slice's weights short-lived (no hoisting
+                    // of later slices' conversions, which spills at 256 registers)
+                    if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                // bf16 operands: code * scale in fp32 (exact), then the top half
+                // of each fp32 is the bf16 value (at most 6 significant bits).
+                float sj[WN][4];
+#pragma unroll
+                for (int s = 0; s < WN; ++s) {
+                    const f32x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, false);
+                    const f32x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bs[s], 1.0f, true);
+                    sj[s][0] = s01[0]; sj[s][1] = s01[1]; sj[s][2] = s23[0]; sj[s][3] = s23[1];
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint4 bq[WN];
+#pragma unroll
+                    for (int s = 0; s < WN; ++s) {
+                        const uint32_t w = j == 0 ? bc[s].x : (j == 1 ? bc[s].y : (j == 2 ? bc[s].z : bc[s].w));
+                        float c[8];
+                        e2m1x8_to_f32(w, c);
+                        const float f = sj[s][j];
+                        bq[s] = make_uint4(pack_pair(c[0] * f, c[1] * f, true), pack_pair(c[2] * f, c[3] * f, true),
+                                           pack_pair(c[4] * f, c[5] * f, true), pack_pair(c[6] * f, c[7] * f, true));
+                    }
+#pragma unroll
+                    for (int ms = 0; ms < MS; ++ms) {
+                        const uint4 a = *reinterpret_cast<const uint4*>(
+                            &sA[buf][(ms * 4 + (j >> 1) * 2) * 1024 + ((j & 1) ? a_slot1 : a_slot0)]);
+#pragma unroll
+                        for (int s = 0; s < WN; ++s)
+                            acc[ms][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bq[s]), acc[ms][s], 0, 0, 0);
+                    }
+                }
+            }
+        };
+
+        u32x4 rc[P][WN], rc2[P][F8 ? WN : 1];
+        uint32_t rs[P][WN];
+#pragma unroll
+        for (int u = 0; u < P - 1; ++u) {
+            issue(u, u, rc[u], rc2[F8 ? u : 0], rs[u]);
+            asm volatile("" ::: "memory");  // keep each step's loads together, in step order
+        }
+        // Step kt waits until only the loads of the P - 2 later steps are in
+        // flight, then refills the buffer freed by step kt - 1. Full groups of P
+        // steps run without branches between them, so every buffer keeps its
+        // registers across the loop; the remaining steps follow after it.
+        // Wave priorities (small tiles whose blocks are all resident at once):
+        // the instruction arbiter favours older waves, so the blocks a CU
+        // received first would stream ahead and the last ones would finish
+        // late, with the chip's loads thinning out meanwhile. Each block's
+        // waves instead run at priority 3, 2, 1, 0 over the four quarters of
+        // their K loop, so blocks that are behind issue first.
+        auto set_prio = [&](int kt) {
+            const int q = (4 * kt) / KT;
+            if (kt != 0 && q == (4 * (kt - 1)) / KT) return;
+            if (q == 0) __builtin_amdgcn_s_setprio(3);
+            else if (q == 1) __builtin_amdgcn_s_setprio(2);
+            else if (q == 2) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        };
+        auto step = [&](int kt, int u) {
+            wait_vmcnt<L * (P - 2)>();
+            bare_barrier();
+            if (BM <= 32 && fair) set_prio(kt);
+#pragma unroll
+            for (int s = 0; s < WN; ++s) {
+                reg_fence(rc[u][s]);
+                reg_fence(rs[u][s]);
+                if (F8) reg_fence(rc2[F8 ? u : 0][s]);
+            }
+            const int nxt = (u + P - 1) % P;  // static once the loops are unrolled
+            issue(kt + P - 1, nxt, rc[nxt], rc2[F8 ? nxt : 0], rs[nxt]);
+            compute(u, rc[u], rc2[F8 ? u : 0], rs[u]);
+        };
+        int kt0 = 0;
+        for (; kt0 + P <= KT; kt0 += P) {
+#pragma unroll
+            for (int u = 0; u < P; ++u) step(kt0 + u, u);
+        }
+#pragma unroll
+        for (int u = 0; u < P - 1; ++u)
+            if (kt0 + u < KT) step(kt0 + u, u);
+        wait_vmcnt<0>();
+        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
+    };
+    if constexpr (BM >= 64) {
+        if (rows > BM / 2) body(std::integral_constant<int, BM / 16>{});
+        else if (BM == 128 && rows > 32) body(std::integral_constant<int, 4>{});
+        else if (rows > 16) body(std::integral_constant<int, 2>{});
+        else body(std::integral_constant<int, 1>{});
+    } else {
+        body(std::integral_constant<int, BM / 16>{});
+    }
 }
 
 // ---- host launchers (device code above) ----

@@ -116,26 +116,6 @@ constexpr int kMiscWords = 2 * kAmaxSlots * kAmaxStride;
 // accumulator T x H exceeds this (half the 256 MB last-level cache).
 constexpr size_t kPhasedYaccBytes = 128ull << 20;
 
-// Sync words of the single-launch layer kernel (u32), cleared by its
-// prologue launch: queue heads and counters on separate 128-byte lines, then
-// per M-tile the FC1 N-blocks done and the FC2-input quantization done, and
-// per (token, FC2 column block of 128) the route contributions stored.
-constexpr int kLayerMaxR = 4096;  // routes of a forward the layer kernel takes
-constexpr int kLsLine = 32;
-constexpr int kLsQueue1 = 0 * kLsLine;  // phase-1 queue head
-constexpr int kLsRouted = 1 * kLsLine;  // route items done
-constexpr int kLsPlan = 2 * kLsLine;    // 1 once the permutation is published
-constexpr int kLsXAmax = 3 * kLsLine;   // x amax items done
-constexpr int kLsXDone = 4 * kLsLine;   // FC1-input quantization items done
-constexpr int kLsFc1All = 5 * kLsLine;  // FC1 tiles done, all M-tiles
-constexpr int kLsHeads = 6 * kLsLine;   // 8 phase-2 queue heads, one line each
-constexpr int kLsFixed = kLsHeads + 8 * kLsLine;
-inline size_t layer_sync_words(int T, int H, int mt_max) {
-    return (size_t)kLsFixed + 2 * (size_t)mt_max + (size_t)T * (size_t)(H / 128);
-}
-// M-tiles of R routes over E experts, at most (the smallest tile, 16 rows).
-inline int layer_mt_bound(int R, int E) { return (R + 15) / 16 + E; }
-
 // The first kWsStatusBytes of a forward's workspace hold its status word:
 // the routing kernel writes 0, or MOE_ERR_INVALID when the prepared blob's
 // header does not match the dimensions of the call; the kernels that read the
@@ -147,7 +127,7 @@ enum WsView {
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
     V_XMXCODES, V_XMXSCALES, V_A2MXCODES, V_A2MXSCALES,  // MXFP4 re-blocked operands
     V_NUM_PUBLIC,
-    V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_YACC, V_SYNC, V_NUM
+    V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_YACC, V_NUM
 };
 
 struct WsPlan {
@@ -201,12 +181,6 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
     }
     p->bytes[V_O] = R * H * 4;
     p->bytes[V_YACC] = (size_t)T * H * 4;
-    if (E <= 256) {
-        // the single-launch layer's counters, sized for min(T, its largest
-        // batch) so that the total never shrinks as T grows
-        const int Tl = T < kLayerMaxR / K ? T : kLayerMaxR / K;
-        p->bytes[V_SYNC] = layer_sync_words(Tl, (int)H, layer_mt_bound(Tl * K, (int)E)) * 4;
-    }
     size_t off = kWsStatusBytes;
     for (int v = 0; v < V_NUM; ++v) {
         p->off[v] = off;

@@ -121,47 +121,4 @@ int report_error(int code, const char* msg);
 hipError_t launch_gemm(int ab, int epi, int bm_index, const GemmArgs& a, hipStream_t s,
                        hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
-// Single-launch layer (moe_layer.hip) for small batches. FC1-input
-// quantization: none (W4A16), MXFP8, NVFP4 with a scale per row (plain or
-// 4-over-6) or per tensor.
-enum LayerXq { LX_NONE = 0, LX_MX8 = 1, LX_NV_ROW = 2, LX_NV_ROW_4O6 = 3, LX_NV_TENSOR = 4 };
-struct LayerArgs {
-    GemmArgs g1, g2;  // FC1 and FC2 as the multi-launch sequence sets them up (g2 not fused)
-    const float* logits;
-    const uint16_t* x;
-    int T, H, I, E, K;
-    int32_t* ids;
-    float* topw;
-    int32_t* counts;
-    int32_t* offsets;
-    int32_t* tiles;  // all kNumBM tile lists
-    int32_t* r2r;
-    int32_t* rt2row;
-    int bmi;  // tile-size index of the GEMMs (g1.tiles is that list)
-    int xq;   // LayerXq
-    uint8_t* xcodes;
-    uint8_t* xscales;
-    float* xg;
-    uint16_t* xdeq;
-    float* a2f;  // NVFP4: the fp32 FC2 input FC1 writes, quantized per M-tile into:
-    uint8_t* a2codes;
-    uint8_t* a2scales;
-    float* a2g;
-    uint16_t* a2deq;
-    uint32_t* misc;  // amax slots
-    uint16_t* y;
-    uint32_t* sync;  // layer_sync_words(T, H, mt_max) words, cleared by the launch's prologue
-    int mt_max;
-    uint32_t* status;
-    long long wait_ticks;  // bound of one wait, in wall-clock ticks (set by launch_layer)
-};
-// Whether the single-launch layer runs this forward (R routes, E experts,
-// tile-size index, mode).
-bool layer_supported(int R, int E, int bm_index, int mode);
-// The prologue (header check, clearing of the sync and misc words) and the
-// layer kernel; t0/t1 time the layer kernel.
-hipError_t launch_layer(const LayerArgs& a, int ab, const void* blob, const BlobHeader& expect,
-                        size_t sync_words, hipStream_t s, hipEvent_t t0 = nullptr,
-                        hipEvent_t t1 = nullptr);
-
 }  // namespace moe

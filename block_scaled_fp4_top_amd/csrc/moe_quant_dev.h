@@ -1,5 +1,5 @@
-// Device helpers of the block quantizers, shared by the quantization kernels
-// and the single-launch layer kernel.
+// Device helpers of the block quantizers (loads of 16 values, wave maximum,
+// fp16 copies of NVFP4 blocks).
 #pragma once
 
 #include "moe_internal.h"

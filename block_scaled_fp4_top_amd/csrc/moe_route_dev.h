@@ -1,5 +1,5 @@
-// Device code of S1 routing and of the permutation scans, shared by the
-// routing kernels and the single-launch layer kernel.
+// Device code of S1 routing (top-K of one token by one wave) and the DPP
+// wave scan of the permutation.
 #pragma once
 
 #include "moe_internal.h"

@@ -78,9 +78,7 @@ typedef enum {
     MOE_ERR_INVALID = 1,     /* null/misaligned pointer, bad size or enum                  */
     MOE_ERR_UNSUPPORTED = 2, /* well-formed but not implemented (e.g. H % 128 != 0)       */
     MOE_ERR_WORKSPACE = 3,   /* workspace or prepared buffer too small                      */
-    MOE_ERR_HIP = 4,         /* a HIP call failed; moe_last_error() has hipGetErrorString */
-    MOE_ERR_TIMEOUT = 5      /* device-side only (moe_forward_status): a bounded wait of the
-                                single-launch layer kernel gave up; y is incomplete          */
+    MOE_ERR_HIP = 4          /* a HIP call failed; moe_last_error() has hipGetErrorString */
 } moe_status;
 
 /* Layer geometry. N1 = 2*I for SwiGLU (rows [0,I) gate, [I,2I) up), I for
@@ -144,35 +142,6 @@ int moe_forward(const moe_dims* d, const void* prepared, size_t prepared_bytes, 
                 int32_t router_weight_on_input, int32_t deterministic_finalize, void* workspace,
                 size_t workspace_bytes, uint16_t* y, hipStream_t stream);
 
-/* Forward paths.
- *   MOE_PATH_MULTI: one launch per stage (route, permute, quantize, FC1,
- *     FC2-input quantization, FC2, finalize), any shape.
- *   MOE_PATH_SINGLE: small batches as one persistent layer kernel (MegaMoE
- *     post, "Our approach"), after a prologue launch that checks the blob
- *     header and clears the kernel's sync counters. Routing, permutation,
- *     both quantizations, both GEMMs and the finalize run as work items of
- *     that one kernel; the FC2 tiles of a group of rows start as soon as its
- *     FC1 tiles are done, and the finalize of a token's columns runs in the
- *     FC2 tile that completes them, in the fixed k order (the deterministic
- *     result, whatever deterministic_finalize says). Every wait in the kernel
- *     is bounded: should one give up, the status word becomes
- *     MOE_ERR_TIMEOUT and y is incomplete. Currently switched off: it did not
- *     finish in two of its modes on the GPU (cause not found), so every shape
- *     fails with MOE_ERR_UNSUPPORTED under this setting.
- *   MOE_PATH_AUTO (default): MOE_PATH_SINGLE where it applies (currently
- *     nowhere), else MULTI. */
-typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_MULTI = 1, MOE_PATH_SINGLE = 2 } moe_path;
-
-/* Process-wide path choice of later moe_forward / moe_forward_noalloc calls
- * (forwards already enqueued keep theirs; a captured graph keeps the path it
- * was captured with). MOE_PATH_SINGLE makes shapes it does not cover fail
- * with MOE_ERR_UNSUPPORTED. */
-int moe_set_forward_path(int32_t path);
-
-/* The path (MOE_PATH_MULTI or MOE_PATH_SINGLE) a forward of this shape takes
- * under the current setting, or a negative moe_status if it would fail. */
-int moe_forward_path(const moe_dims* d, int32_t T, int32_t K, int32_t mode);
-
 /* moe_forward for callers that cannot allocate: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc. The same forward, on a
  * workspace that is a device array inside the library (64 MiB; each GPU the
@@ -195,8 +164,7 @@ int moe_forward_noalloc(const moe_dims* d, const void* prepared, size_t prepared
 /* Status word of the last forward enqueued on `workspace` (synchronous: waits
  * for `stream`, then reads 4 bytes): *status = 0 after a forward whose blob
  * header matched its dimensions, MOE_ERR_INVALID otherwise (y was then not
- * written), MOE_ERR_TIMEOUT after a single-launch forward whose waits gave up
- * (see moe_path). Not for use under graph capture. */
+ * written). Not for use under graph capture. */
 int moe_forward_status(const void* workspace, int32_t* status, hipStream_t stream);
 
 /* S7 alone (unfused finalize, as in PR #5319): y[t][j] = sum_{k<K} w[t][k] *
@@ -245,8 +213,7 @@ int moe_workspace_view(const moe_dims* d, int32_t T, int32_t K, int32_t mode, in
  * synchronises, returns the summed milliseconds per stage since the last
  * reset in ms[0..n) and the number of timed forwards, and resets. Stage ids:
  * 0 route, 1 permute, 2 quantize x, 3 FC1, 4 FC2-input quantize, 5 FC2,
- * 6 finalize, 7 the single-launch layer kernel (a single-launch forward
- * times only stage 0, its prologue launch up to the kernel's start, and 7). */
+ * 6 finalize. */
 int moe_stage_timing(int32_t enable);
 int moe_stage_times(float* ms, int32_t n, int32_t* forwards);
 

@@ -124,30 +124,10 @@ def test_workspace_views(moe):
     assert L.moe_workspace_view(ctypes.byref(d), 16, 2, 0, 99, ctypes.byref(off), ctypes.byref(nb)) == 1
 
 
-def test_forward_path_setting(moe):
-    """The path setting: bad values are refused; while the single-launch layer
-    is switched off every shape resolves to the multi-launch sequence under
-    "auto" and is refused (MOE_ERR_UNSUPPORTED) under "single"."""
-    L = moe._lib
-    d = ctypes.byref(_dims(moe, E=64, H=2048, I=1024))
-    try:
-        assert L.moe_set_forward_path(7) == 1
-        assert L.moe_set_forward_path(0) == 0
-        assert L.moe_forward_path(d, 256, 6, moe.MODES["w4a16"]) == 1
-        assert L.moe_forward_path(d, 0, 6, moe.MODES["w4a16"]) == -1        # T = 0: invalid
-        assert L.moe_set_forward_path(2) == 0
-        assert L.moe_forward_path(d, 256, 6, moe.MODES["w4a16"]) == -2
-        assert L.moe_set_forward_path(1) == 0
-        assert L.moe_forward_path(d, 256, 6, moe.MODES["w4a16"]) == 1
-    finally:
-        L.moe_set_forward_path(0)
-
-
 @pytest.mark.parametrize("E,K", [(64, 6), (256, 8), (8, 2)])
 def test_workspace_never_shrinks_as_tokens_grow(moe, E, K):
     """moe_workspace_bytes(T_max) must cover every forward with T <= T_max,
-    also across the largest batch of the single-launch layer (whose counters
-    the workspace holds up to that batch)."""
+    also across the small-batch permutation threshold (4096 routes)."""
     L = moe._lib
     d = ctypes.byref(_dims(moe, E=E, H=512, I=256))
     prev = 0
