@@ -35,6 +35,7 @@
 
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "moe_internal.h"
 #include "moe_kernels.h"
@@ -217,6 +218,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void reg_fence(uint32_t& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void reg_fence(u32x4& v) { asm volatile("" : "+v"(v)); }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time indexes,
+// e.g. for instruction operands that must be immediates).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // Workgroup barrier without the fence __syncthreads() carries (that fence
 // drains every outstanding load, which would serialise the pipeline). The
 // caller waits for the loads that must have landed; the memory clobber keeps
@@ -380,7 +392,10 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
             const int rr = m < MS * 16 ? s_arow[m] : -1;
             ascsrc = p.a_scales + (size_t)(rr >= 0 ? rr : r_any) * (p.Kdim / 32);
         }
-        constexpr int L = AB_PER_WAVE + (SC ? 1 : 0) + WN * (F8 ? 3 : 2);  // loads per step per wave
+        // loads per step per wave: A, A scales, the strips' weight codes and
+        // one load of all their weight scales
+        static_assert(WN == 2 || WN == 4, "weight scales are read as 2 or 4 strips of a group of 4");
+        constexpr int L = AB_PER_WAVE + (SC ? 1 : 0) + WN * (F8 ? 2 : 1) + 1;
 
         // Weight loads: small M tiles read each weight once, so they stream past
     // the caches (non-temporal); wide tiles rely on L2 hits across the M-tiles
@@ -404,14 +419,29 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     const u32x4* q = reinterpret_cast<const u32x4*>(p.b_codes + tile * kF8TileBytes + lane * 32);
                     c1[s] = load_b(q);
                     c2[s] = load_b(q + 1);
-                    sc[s] = p.b_scales[tile * kF8TileScale + lane];
                 } else if (F4) {
                     c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kF4TileBytes + lane * 16));
-                    sc[s] = p.b_scales[tile * kF4TileScale + lane];
                 } else {
                     c1[s] = load_b(reinterpret_cast<const u32x4*>(p.b_codes + tile * kNvTileBytes + lane * 16));
-                    sc[s] = *reinterpret_cast<const uint32_t*>(
-                        p.b_scales + tile * kNvTileScale + ((lane >> 5) * 16 + (lane & 15)) * 4);
+                }
+            }
+            // the WN strips' scales of this step, side by side in one load:
+            // fp8/fp4 the lane's E8M0 bytes (sc[0], byte s for strip s),
+            // NVFP4 the lane's E4M3 dwords (sc[s])
+            if (SC) {
+                const uint8_t* sp = p.b_scales + wscale_offset(tiles_e, e, gs0, kk, KT, F8 ? kF8TileScale : kF4TileScale,
+                                                               lane, 1);
+                if constexpr (WN == 4) sc[0] = *reinterpret_cast<const uint32_t*>(sp);
+                else sc[0] = *reinterpret_cast<const uint16_t*>(sp);
+            } else {
+                const uint8_t* sp = p.b_scales + wscale_offset(tiles_e, e, gs0, kk, KT, kNvTileScale,
+                                                               (lane >> 5) * 16 + (lane & 15), 4);
+                if constexpr (WN == 4) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(sp);
+                    sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+                } else {
+                    const uint2 v = *reinterpret_cast<const uint2*>(sp);
+                    sc[0] = v.x; sc[1] = v.y;
                 }
             }
         };
@@ -436,12 +466,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     const uint4 a0 = *reinterpret_cast<const uint4*>(&sA[buf][ms * 1024 + lane * 16]);
                     const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w, 0, 0, 0, 0};
                     const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
-#pragma unroll
-                    for (int s = 0; s < WN; ++s) {
+                    static_for<WN>([&](auto S) {
+                        constexpr int s = decltype(S)::value;
                         const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w, 0, 0, 0, 0};
+                        // byte s of the packed weight scales (operand select)
                         acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bv, acc[ms][s], 4, 4, 0, asc, 0, (int)bs[s]);
-                    }
+                            av, bv, acc[ms][s], 4, 4, 0, asc, s, (int)bs[0]);
+                    });
                 }
             } else if (F8) {
 #pragma unroll
@@ -451,13 +482,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
                     const i32x8 av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                                       (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
                     const int asc = (int)((sAsc[buf][ms * 16 + (lane & 15)] >> (8 * (lane >> 4))) & 0xFFu);
-#pragma unroll
-                    for (int s = 0; s < WN; ++s) {
+                    static_for<WN>([&](auto S) {
+                        constexpr int s = decltype(S)::value;
                         const i32x8 bv = {(int)bc[s].x, (int)bc[s].y, (int)bc[s].z, (int)bc[s].w,
                                           (int)bc2[s].x, (int)bc2[s].y, (int)bc2[s].z, (int)bc2[s].w};
                         acc[ms][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            av, bv, acc[ms][s], 0, 0, 0, asc, 0, (int)bs[s]);
-                    }
+                            av, bv, acc[ms][s], 0, 0, 0, asc, s, (int)bs[0]);
+                    });
                 }
             } else if (!BF) {
                 // fp16 operands: each E2M1 pair converts to two fp16 values, then
@@ -564,7 +595,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int s = 0; s < WN; ++s) {
                 reg_fence(rc[u][s]);
-                reg_fence(rs[u][s]);
+                if (!SC || s == 0) reg_fence(rs[u][s]);
                 if (F8) reg_fence(rc2[F8 ? u : 0][s]);
             }
             const int nxt = (u + P - 1) % P;  // static once the loops are unrolled

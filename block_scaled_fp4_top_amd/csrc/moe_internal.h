@@ -31,7 +31,7 @@ constexpr int kMaxE = 1024;
 constexpr int kMaxK = 64;
 constexpr uint32_t kBlobMagic0 = 0x5746454Du;  // "MEFW"
 constexpr uint32_t kBlobMagic1 = 0x34504634u;  // "4FP4"
-constexpr uint32_t kBlobVersion = 1;
+constexpr uint32_t kBlobVersion = 2;
 constexpr size_t kBlobHeader = 4096;
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -54,6 +54,12 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 //    n = l % 16, q = l / 16; byte b < 16 is k = 16 q + b, byte b >= 16 is
 //    k = 64 + 16 q + (b - 16). Scales: byte l is the E8M0 scale of row l % 16
 //    for 32-block l / 16 of the tile.
+// Scales are not stored per micro-tile but per group of four strips
+// (kScaleGroup) and K step: one block of 4 x (a micro-tile's scale bytes) in
+// which each lane's scale units of the four strips lie side by side (unit:
+// the lane's E8M0 byte for MXFP8 and MXFP4, its dword of four E4M3 bytes for
+// NVFP4), so a wave reads the scales of its 2 or 4 strips for one K step with
+// one load (wscale_offset).
 // SwiGLU W1 rows are interleaved by strips of 16: prepared strip 2s holds gate
 // rows [16 s, 16 s + 16) and strip 2s + 1 the up rows I + [16 s, 16 s + 16), so
 // one wave sees matching gate/up accumulators in the same lanes.
@@ -62,6 +68,17 @@ struct BlobHeader {
     int32_t E, H, I, N1, act, pad0;
     uint64_t off_g1, off_g2, off_amax, off_w1, off_s1, off_w2, off_s2, total;
 };
+
+constexpr int kScaleGroup = 4;
+// Byte offset of scale unit `unit_index` (tile-local numbering as above) of
+// strip nt, K step kt, expert e, in one matrix family's scale array
+// (expert_tiles micro-tiles per expert, KT steps, tile_scale_bytes per tile).
+__host__ __device__ inline size_t wscale_offset(size_t expert_tiles, int e, int nt, int kt, int KT,
+                                                int tile_scale_bytes, int unit_index, int unit_bytes) {
+    return (size_t)e * expert_tiles * tile_scale_bytes +
+           ((size_t)(nt / kScaleGroup) * KT + kt) * (size_t)(kScaleGroup * tile_scale_bytes) +
+           (size_t)unit_index * (kScaleGroup * unit_bytes) + (size_t)(nt % kScaleGroup) * unit_bytes;
+}
 
 struct BlobLayout {
     BlobHeader h;

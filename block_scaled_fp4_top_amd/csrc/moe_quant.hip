@@ -321,7 +321,8 @@ __global__ __launch_bounds__(256) void prep_nvfp4_kernel(const float* __restrict
     const int l1 = (p & 15) + 16 * (2 * half), l2 = l1 + 16;
     *reinterpret_cast<uint32_t*>(cb + l1 * 16 + j * 4) = packed[0];
     *reinterpret_cast<uint32_t*>(cb + l2 * 16 + j * 4) = packed[1];
-    scales[tile * kNvTileScale + (half * 16 + (p & 15)) * 4 + j] = (uint8_t)sf;
+    scales[wscale_offset(tiles_e, e, p / kStrip, kt, K / kTileK, kNvTileScale, half * 16 + (p & 15), 4) + j] =
+        (uint8_t)sf;
 }
 
 // One thread per (expert, prepared row, 32-block).
@@ -357,7 +358,8 @@ __global__ __launch_bounds__(256) void prep_mxfp8_kernel(const float* __restrict
     const int la = (p & 15) + 16 * q0, lb = la + 16;
     *reinterpret_cast<uint4*>(cb + la * 32 + boff) = *reinterpret_cast<const uint4*>(c);
     *reinterpret_cast<uint4*>(cb + lb * 32 + boff) = *reinterpret_cast<const uint4*>(c + 16);
-    scales[tile * kF8TileScale + (p & 15) + 16 * kb4] = (uint8_t)e8;
+    scales[wscale_offset(tiles_e, e, p / kStrip, kt, K / kTileK, kF8TileScale, (p & 15) + 16 * kb4, 1)] =
+        (uint8_t)e8;
 }
 
 // One thread per (expert, prepared row, 32-block): the two 16-blocks NVFP4-
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(256) void prep_mxfp4_kernel(const float* __restrict
     const size_t tile = (size_t)e * tiles_e + (size_t)(p / kStrip) * (K / kTileK) + kt;
     const int lane = (p & 15) + 16 * q;
     *reinterpret_cast<uint4*>(codes + tile * kF4TileBytes + lane * 16) = make_uint4(mx[0], mx[1], mx[2], mx[3]);
-    scales[tile * kF4TileScale + lane] = (uint8_t)e8;
+    scales[wscale_offset(tiles_e, e, p / kStrip, kt, K / kTileK, kF4TileScale, lane, 1)] = (uint8_t)e8;
 }
 
 __global__ void write_header_kernel(BlobHeader h, uint32_t* __restrict__ dst) {

@@ -120,10 +120,21 @@ def _logical_rows(N, swiglu_I):
     return (st & 1) * swiglu_I + (st >> 1) * 16 + (p & 15)
 
 
+def tile_scales(scales_b: np.ndarray, NT: int, KT: int, unit: int) -> np.ndarray:
+    """One expert's weight-scale bytes as stored (per group of four 16-row
+    strips and K step, each lane's scale units of the four strips side by
+    side; unit = 1 byte for MXFP8/MXFP4, 4 bytes for NVFP4) -> the same bytes
+    in micro-tile order [NT][KT][tile scale bytes]."""
+    S = 64 if unit == 1 else 128
+    b = scales_b.reshape(NT // 4, KT, S // unit, 4, unit)   # group, step, unit, strip in group, byte
+    return np.ascontiguousarray(b.transpose(0, 3, 1, 2, 4)).reshape(-1)
+
+
 def unpack_nvfp4_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: int, swiglu_I=0):
     """Blob bytes of one expert's NVFP4 matrix -> (codes [N][K], scales [N][K/16])
     in logical (checkpoint) order."""
     NT, KT = N // 16, K // 128
+    scales_b = tile_scales(scales_b, NT, KT, 4)
     t = codes_b.reshape(NT, KT, 64, 4, 4)           # tile, lane, dword j, byte
     lo, hi = t & 15, t >> 4
     nib = np.stack([lo, hi], axis=-1).reshape(NT, KT, 64, 4, 8)  # element e = 2*byte + half
@@ -153,6 +164,7 @@ def unpack_nvfp4_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: in
 
 def unpack_mxfp8_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: int, swiglu_I=0):
     NT, KT = N // 16, K // 128
+    scales_b = tile_scales(scales_b, NT, KT, 1)
     t = codes_b.reshape(NT, KT, 4, 16, 32)          # tile, q, row, byte
     out = np.empty((N, K), np.uint8)
     ov = out.reshape(NT, 16, KT, 128)
@@ -177,6 +189,7 @@ def unpack_mxfp4_matrix(codes_b: np.ndarray, scales_b: np.ndarray, N: int, K: in
     """MXFP4 micro-tiles: lane l = row (l % 16) + 16 q holds 16 bytes = the row's
     32-block q of the tile (even element in the low nibble); scale byte l."""
     NT, KT = N // 16, K // 128
+    scales_b = tile_scales(scales_b, NT, KT, 1)
     t = codes_b.reshape(NT, KT, 4, 16, 16)          # tile, q, row, byte
     nib = np.stack([t & 15, t >> 4], axis=-1).reshape(NT, KT, 4, 16, 32)
     out = np.empty((N, K), np.uint8)

@@ -135,3 +135,23 @@ def test_workspace_never_shrinks_as_tokens_grow(moe, E, K):
         b = L.moe_workspace_bytes(d, T, K, moe.MODES["w4a16"])
         assert b >= prev, (T, b, prev)
         prev = b
+
+
+@pytest.mark.parametrize("unit,S", [(1, 64), (4, 128)])
+def test_weight_scale_layout_round_trip(unit, S):
+    """The test unpackers' view of the stored weight-scale layout: byte b of
+    unit u of strip nt at K step kt lives at ((nt // 4) * KT + kt) * 4 S +
+    u * 4 unit + (nt % 4) * unit + b (group of four strips per step, the
+    strips' units side by side); tile_scales restores micro-tile order."""
+    from tests.helpers import tile_scales
+    import numpy as np
+    NT, KT = 8, 3
+    tiles = np.arange(NT * KT * S, dtype=np.int64).reshape(NT, KT, S) % 251
+    stored = np.zeros(NT * KT * S, np.int64)
+    for nt in range(NT):
+        for kt in range(KT):
+            for u in range(S // unit):
+                for b in range(unit):
+                    off = ((nt // 4) * KT + kt) * 4 * S + u * 4 * unit + (nt % 4) * unit + b
+                    stored[off] = tiles[nt, kt, u * unit + b]
+    assert np.array_equal(tile_scales(stored, NT, KT, unit).reshape(NT, KT, S), tiles)
