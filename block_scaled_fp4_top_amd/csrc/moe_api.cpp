@@ -441,11 +441,11 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     g2.I = I;
     g2.topw = topw;
     g2.out_f32 = WS(float, V_O);
-    g2.yacc = WS(float, V_YACC);
-    g2.fused = fused;
-    // a token accumulator well above the 256 MB last-level cache: N-block-major
-    // FC2 order, so each phase's atomics stay in cache
-    g2.phased = fused && (size_t)T * H * 4 > kPhasedYaccBytes;
+    g2.fused = fused ? FUSE_ARRIVE : FUSE_NONE;
+    g2.arrive = WS(uint32_t, V_ARRIVE);
+    g2.o_rows = R;
+    g2.rt2row = rt2row;
+    g2.y = y;
     g2.status = status;
 
     // while stage timing is on, the timer state belongs to this forward
@@ -497,13 +497,12 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
                     "re-block FC2 input");
     }
 
-    if (fused) HIP_TRY(launch_fill_u32(WS(uint32_t, V_YACC), (size_t)T * H, 0u, stream), "zero y_acc");
+    if (fused)
+        HIP_TRY(launch_fill_u32(WS(uint32_t, V_ARRIVE), (size_t)T * (H / 128), 0u, stream), "zero arrival counters");
     timer_kernel_events(tslot, 5, &t0, &t1);
     HIP_TRY(launch_gemm(ab, EPI_FC2, bmi, g2, stream, t0, t1), "FC2");
 
-    if (fused) {
-        HIP_TRY(launch_yacc_to_bf16(WS(float, V_YACC), (size_t)T * H, y, status, stream), "convert y");
-    } else {
+    if (!fused) {
         HIP_TRY(launch_finalize(WS(float, V_O), 0, rt2row, router_weight_on_input ? nullptr : topw, T, K, H,
                                 y, status, stream),
                 "finalize");

@@ -29,8 +29,8 @@
 //    input-side router weight in FP32, then the FC2 input: fp32 (+ partial
 //    maxima of |value| for the per-tensor global scale) for
 //    NVFP4, bf16 for W4A16, or MXFP8 codes and scales quantized in place;
-//    FC2: store of the permuted output or fp32 atomic scatter-add into the
-//    token accumulator (fused finalize).
+//    FC2: store of the permuted output O, and for the fused finalize the
+//    reduction of every token whose K routes this block completes.
 #include <hip/hip_ext.h>
 
 #include <atomic>
@@ -76,7 +76,7 @@ __device__ __forceinline__ float row16_max(float v) {
 template <int AB, int MS, int WN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS][WN], int e,
                                               int row0, int rows, const int* s_arow, int gs0,
-                                              int lane) {
+                                              int lane, int nb, int bn) {
     const float gw = p.b_g ? p.b_g[e] : 1.0f;
     const int c16 = lane & 15;
     if constexpr (EPI == EPI_FC1 && AB == AB_FP8) {
@@ -167,13 +167,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                     }
                 }
             } else {
-                if (p.fused) {
-                    const int route = p.row_to_route[row];
-                    const int t = route / p.topk;
-                    const float w = p.on_input ? 1.0f : p.topw[route];
+                if (p.fused == FUSE_ARRIVE) {
+                    // N-block-major O, with device scope: rows are read back by
+                    // a block on any XCD
+                    float* o = p.out_f32 + ((size_t)nb * p.o_rows + row) * bn + (gs0 * 16 - nb * bn) + c16;
 #pragma unroll
                     for (int s = 0; s < WN; ++s)
-                        atomicAdd(&p.yacc[(size_t)t * p.N + (gs0 + s) * 16 + c16], w * (acc[ms][s][i] * sc));
+                        __hip_atomic_store(o + s * 16, acc[ms][s][i] * sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 } else {
 #pragma unroll
                     for (int s = 0; s < WN; ++s)
@@ -235,6 +235,86 @@ __device__ __forceinline__ void static_for(F&& f) {
 // the compiler from moving memory accesses across.
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Fused finalize by arrival counts, after a block has stored its O tile
+// (rows of one expert's M-tile, the BN columns of N-block nb). Each route of
+// the tile counts itself in on its token's counter for this N-block; the
+// route whose increment completes the count (the K-th) hands its token to the
+// block, which then reduces the token's K rows of O over these BN columns in
+// the order k = 0..K-1, each term weighted by the router weight (output side),
+// in fp32 with one rounding to bf16 at the end. That is the deterministic
+// finalize's arithmetic in its order, so both variants give the same bits, and
+// no fp32 atomics touch the output: a token's columns are written once, by
+// whichever block arrives last.
+// O is stored N-block-major ([N / BN][R][BN]) in this mode, so that the rows
+// of one N-block form one contiguous region. The wide tiles' block order
+// gives each XCD a contiguous range of (N-block, M-tile) pairs, so the blocks
+// of an N-block, hence the writers and the reader of a token's rows for it,
+// mostly share one L2 (an N-block-major order over the whole chip ran this
+// FC2 1.5x slower at 16k tokens: 5.57 against 3.79 ms).
+// Visibility across XCDs (each has its own L2) uses device-scope accesses on
+// the O rows themselves rather than device-scope fences, which write back or
+// invalidate a whole L2 (measured: 3x slower FC2 at 16k tokens, 9x on the
+// decode tiles): the epilogue stores O with device scope, so each store is
+// complete only once it is visible device-wide; every wave waits for its
+// stores before the barrier that precedes the block's counter increments; and
+// the block that completes a count reads the rows back with device-scope
+// loads, issued after its increment has returned.
+template <int NW, int BN>
+__device__ __forceinline__ void arrive_finalize(const GemmArgs& p, int nb, int row0, int rows,
+                                                int* s_list, int* s_n) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int K = p.topk, NB = p.N / BN;
+    wait_vmcnt<0>();  // this wave's O stores are complete
+    __syncthreads();  // ... and every wave's; s_n was zeroed before the main loop
+    for (int m = tid; m < rows; m += NW * 64) {
+        const int t = p.row_to_route[row0 + m] / K;
+        const uint32_t old = __hip_atomic_fetch_add(p.arrive + (size_t)t * NB + nb, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (old == (uint32_t)(K - 1)) s_list[atomicAdd(s_n, 1)] = t;
+    }
+    __syncthreads();
+    const int n = *s_n;
+    constexpr int CPL = BN / 64;  // columns per lane: lane + 64 j, coalesced per load
+    const float* ob = p.out_f32 + (size_t)nb * p.o_rows * BN + lane;  // this N-block's part of O
+    const int c0 = nb * BN + lane;
+    for (int j = wave; j < n; j += NW) {
+        const int t = s_list[j];
+        // lane k < K holds route k's row and weight; the loads of up to 8
+        // routes are issued together, then summed in k order (the block's
+        // tail is latency, not bandwidth: one block per CU)
+        const int kl = lane < K ? lane : 0;
+        const int my_row = p.rt2row[(size_t)t * K + kl];
+        const float my_w = p.on_input ? 1.0f : p.topw[(size_t)t * K + kl];
+        float a[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) a[c] = 0.0f;
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float q[8][CPL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k0 + u < K) {
+                    const int row = __builtin_amdgcn_readlane(my_row, k0 + u);
+                    const float* o = ob + (size_t)row * BN;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c)
+                        q[u][c] = __hip_atomic_load(o + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (k0 + u < K) {
+                    const float w = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k0 + u));
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) a[c] = __fmaf_rn(w, q[u][c], a[c]);
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) p.y[(size_t)t * p.N + c0 + 64 * c] = bf16_rne(a[c]);
+    }
+}
+
 // Grouped GEMM tile kernel. P-stage software pipeline over 128-deep K steps:
 // while step kt is multiplied, the loads of steps kt+1 .. kt+P-1 are in
 // flight (A into P rotating LDS buffers by direct loads, B into P rotating
@@ -254,6 +334,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(256))) uint32_t sAsc[P][SC ? (BM > 64 ? BM : 64) : 1];
     __shared__ __attribute__((aligned(1024))) uint8_t sJunk[1024];
     __shared__ int s_arow[BM];
+    __shared__ int s_narrive;  // fused finalize by arrival counts: tokens this block completes
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar registers
@@ -268,12 +349,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     //    columns in its L2 (re-read by the M-tiles of an expert), and the eight
     //    XCDs walk the A rows in step, so the last-level cache serves most A
     //    re-reads.
-    //  - Wide tiles, FC2 with the fused finalize into a token accumulator larger
-    //    than the last-level cache: N-block slowest for the whole chip (every
-    //    XCD takes one contiguous range of M-tiles per N-block), so the
-    //    atomics of a phase land on one N-block's columns of the accumulator
-    //    (T x 512 x 4 bytes), which stay cache-resident; an expert's M-tiles
-    //    still share one XCD's L2 for their weights.
     //  - Small tiles (every weight is read once): the active (M-tile, N-block)
     //    pairs, N-block fastest, are cut into 8 contiguous ranges, one per XCD.
     //    All N-blocks of an M-tile then run on one XCD, so its A rows come into
@@ -290,15 +365,6 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         mt = w / NB;
         nb = w % NB;
         fair = work <= p.resident;
-    } else if (EPI == EPI_FC2 && p.phased) {
-        const int NB = p.N / (16 * NW * WN);
-        const int act = p.tiles[p.E];
-        const int per = (act + 7) >> 3;
-        if (per == 0) return;  // no rows (a forward always has some)
-        const int j = blockIdx.x >> 3;
-        nb = j / per;
-        mt = (blockIdx.x & 7) * per + j % per;
-        if (nb >= NB || mt >= act) return;
     } else {
         const int id = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
         mt = id % p.mt_max;
@@ -333,6 +399,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
     if (status) return;  // blob prepared for other dimensions: no weight reads, no stores
     for (int m = tid; m < BM; m += NW * 64)
         s_arow[m] = m < rows ? (p.gather ? p.row_to_route[row0 + m] / p.topk : row0 + m) : -1;
+    if (tid == 0) s_narrive = 0;
     __syncthreads();
 
     // Main loop and epilogue of one tile whose rows fit in MS 16-row groups
@@ -611,7 +678,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         for (int u = 0; u < P - 1; ++u)
             if (kt0 + u < KT) step(kt0 + u, u);
         wait_vmcnt<0>();
-        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
+        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane, nb, 16 * NW * WN);
     };
     if constexpr (BM >= 64) {
         if (rows > BM / 2) body(std::integral_constant<int, BM / 16>{});
@@ -620,6 +687,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         else body(std::integral_constant<int, 1>{});
     } else {
         body(std::integral_constant<int, BM / 16>{});
+    }
+    if constexpr (EPI == EPI_FC2) {
+        if (p.fused == FUSE_ARRIVE) {
+            __syncthreads();  // s_arow is the list of completed tokens from here on
+            arrive_finalize<NW, 16 * NW * WN>(p, nb, row0, rows, s_arow, &s_narrive);
+        }
     }
 }
 
@@ -657,9 +730,7 @@ static int resident_blocks() {
 
 template <int AB, int EPI, int BM, int WN, int P, int NW>
 static void launch_cfg(const GemmArgs& a, hipStream_t s, hipEvent_t t0, hipEvent_t t1) {
-    long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
-    if (BM > 32 && EPI == EPI_FC2 && a.phased)  // room for 8 ranges of ceil(mt_max / 8) per N-block
-        blocks = 8LL * (a.N / (16 * NW * WN)) * ((a.mt_max + 7) / 8);
+    const long long blocks = (long long)(a.N / (16 * NW * WN)) * a.mt_max;
     const dim3 grid((unsigned)((blocks + 7) / 8 * 8)), block(NW * 64);
     GemmArgs b = a;
     b.resident = resident_blocks<AB, BM, WN, EPI, P, NW>();

@@ -129,10 +129,6 @@ constexpr int kAmaxSlots = 32, kAmaxStride = 32;
 constexpr int kMiscXAmax = 0, kMiscA2Amax = kAmaxSlots * kAmaxStride;
 constexpr int kMiscWords = 2 * kAmaxSlots * kAmaxStride;
 
-// The fused FC2 switches to its N-block-major block order when the fp32 token
-// accumulator T x H exceeds this (half the 256 MB last-level cache).
-constexpr size_t kPhasedYaccBytes = 128ull << 20;
-
 // The first kWsStatusBytes of a forward's workspace hold its status word:
 // the routing kernel writes 0, or MOE_ERR_INVALID when the prepared blob's
 // header does not match the dimensions of the call; the kernels that read the
@@ -144,7 +140,7 @@ enum WsView {
     V_XCODES, V_XSCALES, V_XG, V_A2F, V_A2CODES, V_A2SCALES, V_A2G, V_O,
     V_XMXCODES, V_XMXSCALES, V_A2MXCODES, V_A2MXSCALES,  // MXFP4 re-blocked operands
     V_NUM_PUBLIC,
-    V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_YACC, V_NUM
+    V_TILES = V_NUM_PUBLIC, V_BHIST, V_MISC, V_XDEQ, V_A2DEQ, V_ARRIVE, V_NUM
 };
 
 struct WsPlan {
@@ -197,7 +193,9 @@ inline void plan_workspace(const moe_dims& d, int T, int K, int mode, WsPlan* p)
         p->bytes[V_A2F] = R * I * 2;  // bf16 FC2 input
     }
     p->bytes[V_O] = R * H * 4;
-    p->bytes[V_YACC] = (size_t)T * H * 4;
+    // fused finalize: one arrival counter per token and FC2 N-block (N-blocks
+    // are at least 128 columns wide)
+    p->bytes[V_ARRIVE] = (size_t)T * (H / 128) * 4;
     size_t off = kWsStatusBytes;
     for (int v = 0; v < V_NUM; ++v) {
         p->off[v] = off;

@@ -46,8 +46,6 @@ hipError_t launch_reblock_mxfp4(const uint8_t* nv_codes, const uint8_t* nv_scale
                                 hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // status: the forward's status word (skip all work when not 0), or null.
-hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, const uint32_t* status,
-                               hipStream_t s);
 hipError_t launch_finalize(const void* O, int is_bf16, const int32_t* rt2row, const float* w,
                            int T, int K, int H, uint16_t* y, const uint32_t* status,
                            hipStream_t s);
@@ -68,6 +66,10 @@ hipError_t launch_prep_mxfp8(const float* w, int E, int N, int K, int swiglu_I, 
 // AB_FP4: MXFP4 operands (re-blocked NVFP4) on the block-scaled matrix cores.
 enum GemmAB { AB_F16_NV = 0, AB_BF16_NV = 1, AB_FP8 = 2, AB_FP4 = 3 };
 enum GemmEpi { EPI_FC1 = 0, EPI_FC2 = 1 };
+// How FC2 finishes the layer: store O for the finalize kernel, or store O and
+// let the block that completes a token's K routes for its columns reduce them
+// into y (arrival counts).
+enum GemmFuse { FUSE_NONE = 0, FUSE_ARRIVE = 1 };
 
 struct GemmArgs {
     // A: activations. gather != 0: A row of permuted row r is row_to_route[r] / topk.
@@ -97,9 +99,12 @@ struct GemmArgs {
     uint8_t* a2_codes;   // FC1 MXFP8: FC2-input E4M3 codes [R][I], quantized here
     uint8_t* a2_scales;  //            and their E8M0 block scales [R][I/32]
     uint32_t* amax_slot; // FC1: kAmaxSlots partial maxima of the FC2 input, kAmaxStride apart (NVFP4 per-tensor)
-    float* yacc;         // FC2 fused: [T][N]
-    int fused;
-    int phased;          // FC2 fused on wide tiles: N-block-major block order (large y_acc)
+    int fused;           // FC2: FUSE_NONE or FUSE_ARRIVE
+    uint32_t* arrive;    // FC2 fused by arrival counts: [T][N / block columns] counters, zero on entry;
+                         //   O is then N-block-major, [N / BN][R][BN] for block columns BN
+    int o_rows;          //   R, the rows of O
+    const int32_t* rt2row;  //   route (t, k) -> its row of O
+    uint16_t* y;         //   bf16 output [T][N]
     const uint32_t* status;  // the forward's status word: blocks exit when it is not 0
 };
 

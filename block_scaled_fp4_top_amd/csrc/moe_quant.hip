@@ -187,19 +187,6 @@ __global__ void fill_u32_kernel(uint32_t* __restrict__ p, size_t n, uint32_t v) 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef uint32_t vu2 __attribute__((ext_vector_type(2)));
 
-// y = bf16(y_acc), four elements per thread and step; y_acc is read once, so
-// its loads are non-temporal.
-__global__ void yacc_to_bf16_kernel(const float* __restrict__ yacc, size_t n4,
-                                    uint16_t* __restrict__ y, const uint32_t* __restrict__ status) {
-    if (status && *status) return;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
-        const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(yacc) + i);
-        reinterpret_cast<uint2*>(y)[i] =
-            make_uint2((uint32_t)bf16_rne(v.x) | ((uint32_t)bf16_rne(v.y) << 16),
-                       (uint32_t)bf16_rne(v.z) | ((uint32_t)bf16_rne(v.w) << 16));
-    }
-}
-
 // Deterministic finalize: one block per token and column chunk (blockIdx.y;
 // the whole row when gridDim.y == 1); the token's K route rows and weights are
 // staged in LDS, each thread reduces 4 columns over k = 0..K-1 in order in
@@ -488,14 +475,6 @@ hipError_t launch_reblock_mxfp4(const uint8_t* nv_codes, const uint8_t* nv_scale
 
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
     hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 8192)), dim3(256), 0, s, p, n, v);
-    return hipGetLastError();
-}
-
-hipError_t launch_yacc_to_bf16(const float* yacc, size_t n, uint16_t* y, const uint32_t* status,
-                               hipStream_t s) {
-    // n = T * H is a multiple of 128 (H is)
-    hipLaunchKernelGGL(yacc_to_bf16_kernel, dim3(grid_for(n / 4, 8192)), dim3(256), 0, s, yacc, n / 4, y,
-                       status);
     return hipGetLastError();
 }
 

@@ -130,8 +130,9 @@ size_t moe_workspace_bytes(const moe_dims* d, int32_t T_max, int32_t K, int32_t 
  *   the FC2-input quantization or bf16 store; finalize weights 1).
  *   deterministic_finalize: 1 = FC2 stores the permuted output O in fp32, then
  *   a fixed-order unpermute+reduce in fp32 (bit-identical run to run);
- *   0 = fused scatter-add in the FC2 epilogue (fp32 atomics; the summation
- *   order, hence the last bits, may vary run to run).
+ *   0 = the finalize fused into the FC2 kernel: the FC2 block that completes
+ *   a token's K routes for its output columns reduces them, in the same order
+ *   and arithmetic, so the output is the same bits as with 1.
  *   MXFP8 quantizes the FC2 input in the FC1 epilogue (no fp32 copy).
  *   workspace: >= moe_workspace_bytes(d, T, K, mode) bytes, 256-byte aligned;
  *   afterwards it holds the forward's status word (first 4 bytes) and the
@@ -198,7 +199,8 @@ int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8
  *   6 x codes                    7 x scales               8 x global scale(s) f32
  *   9 FC2 input, fp32 before quantization [R][I] (W4A4) or bf16 (W4A16)
  *   10 FC2-input codes           11 FC2-input scales      12 FC2-input global scale(s)
- *   13 permuted FC2 output O [R][H] f32 (deterministic finalize)
+ *   13 permuted FC2 output O [R][H] f32 (deterministic finalize; after a
+ *      fused forward the view holds O in a column-blocked order)
  *   14/15 x re-blocked to MXFP4: codes [T][H/2], E8M0 scales [T][H/32] (mode 5)
  *   16/17 FC2 input re-blocked to MXFP4: codes [R][I/2], scales [R][I/32] (mode 5)
  * Returns MOE_ERR_INVALID for a view the mode does not produce. */

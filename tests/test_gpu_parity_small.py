@@ -225,8 +225,8 @@ def test_deterministic_repeat_and_graph_replay(mode):
 
 @pytest.mark.parametrize("mode", ["w4a4_tensor", "mxfp8"])
 def test_fused_graph_replay(mode):
-    """Fused finalize under graph capture: the accumulator is cleared by a
-    kernel inside the graph on every replay."""
+    """Fused finalize under graph capture: the arrival counters are cleared
+    by a kernel inside the graph on every replay."""
     T, H, I, E, K = 24, 256, 128, 8, 3
     inp = Inputs(T, H, I, E, K, "swiglu", "normal")
     d = moe.Dims(E, H, I, "swiglu", _fmt(mode))
@@ -250,18 +250,45 @@ def test_fused_graph_replay(mode):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert_output_close(bf16_to_f64(y), bf16_to_f64(yd), f"fused graph replay {rep}")
+        assert torch.equal(y, yd), f"fused graph replay {rep}"
 
 
 def test_fused_matches_deterministic():
+    """The fused finalize reduces each token's K routes in the deterministic
+    finalize's order and arithmetic: the two outputs are the same bits."""
     T, H, I, E, K = 32, 256, 128, 8, 4
     inp = Inputs(T, H, I, E, K, "swiglu", "normal")
     for mode in MODES:
+        print(f"case mode={mode}", flush=True)
         d = moe.Dims(E, H, I, "swiglu", _fmt(mode))
         blob = moe.prepare_weights(d, inp.w1, inp.w2)
-        yd = bf16_to_f64(moe.forward(d, blob, inp.x, inp.logits, K, mode, False, True))
-        yf = bf16_to_f64(moe.forward(d, blob, inp.x, inp.logits, K, mode, False, False))
-        assert_output_close(yf, yd, f"fused vs det {mode}")
+        yd = moe.forward(d, blob, inp.x, inp.logits, K, mode, False, True)
+        yf = moe.forward(d, blob, inp.x, inp.logits, K, mode, False, False)
+        torch.cuda.synchronize()
+        assert torch.equal(yf, yd), f"fused vs det {mode}"
+
+
+@pytest.mark.parametrize("mode,on_input", [("mxfp8", False), ("w4a4_token", True), ("w4a16", False)])
+def test_fused_on_reused_workspace(mode, on_input):
+    """Fused forwards of different inputs, then a smaller one, on one
+    workspace: the rows of O a completing block reads back are this call's
+    (a stale row from the call before would change the sum), and the arrival
+    counters start from zero on every call."""
+    H, I, E = 512, 256, 16
+    d = None
+    ws = None
+    for i, (T, K) in enumerate([(96, 4), (96, 4), (40, 3), (96, 4)]):
+        print(f"case mode={mode} call={i} T={T} K={K}", flush=True)
+        inp = Inputs(T, H, I, E, K, "swiglu", "normal", seed=100 + i)
+        if d is None:
+            d = moe.Dims(E, H, I, "swiglu", _fmt(mode))
+            blob = moe.prepare_weights(d, inp.w1, inp.w2)
+            ws = torch.empty(moe.workspace_bytes(d, 96, 4, mode), dtype=torch.uint8, device="cuda")
+        yf = moe.forward(d, blob, inp.x, inp.logits, K, mode, on_input, False, workspace=ws)
+        torch.cuda.synchronize()
+        yd = moe.forward(d, blob, inp.x, inp.logits, K, mode, on_input, True)
+        torch.cuda.synchronize()
+        assert torch.equal(yf, yd), f"call {i}: fused vs det {mode}"
 
 
 @pytest.mark.parametrize("T,K,H", [(37, 5, 384), (9, 3, 2052), (2100, 2, 260)])

@@ -1,9 +1,8 @@
 """The forward without allocation (moe_forward_noalloc), called through the C
 ABI, against moe_forward on a caller workspace: bit-identical outputs with
-the deterministic finalize and within the output bar with the fused one, on
-two calls in a row where the second has fewer tokens (the built-in workspace
+either finalize (the fused one reduces in the deterministic order), on two
+calls in a row where the second has fewer tokens (the built-in workspace
 keeps the first call's contents)."""
-import numpy as np
 import pytest
 import torch
 
@@ -13,7 +12,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import block_scaled_fp4_top_amd as moe  # noqa: E402
-from tests.helpers import Inputs, assert_output_close, bf16_to_f64  # noqa: E402
+from tests.helpers import Inputs  # noqa: E402
 
 CASES = [  # mode, act, on_input, (T_first, T_second), E, H, I, K
     ("w4a16", "swiglu", False, (256, 37), 64, 2048, 1024, 6),
@@ -39,11 +38,8 @@ def test_noalloc_matches_workspace_forward(case):
             torch.cuda.synchronize()
             outs.append((y_na.clone(), y_ws.clone()))
         for (y_na, y_ws), inp in zip(outs, (big, small)):
-            if det:
-                assert torch.equal(y_na.view(torch.int16), y_ws.view(torch.int16)), \
-                    f"{mode} T={inp.T}: no-alloc forward differs from the workspace forward"
-            else:
-                assert_output_close(bf16_to_f64(y_na), bf16_to_f64(y_ws), f"{mode} fused T={inp.T}")
+            assert torch.equal(y_na.view(torch.int16), y_ws.view(torch.int16)), \
+                f"{mode} det={det} T={inp.T}: no-alloc forward differs from the workspace forward"
 
 
 def test_noalloc_rejects_oversized_forward():
