@@ -277,41 +277,64 @@ __device__ __forceinline__ void arrive_finalize(const GemmArgs& p, int nb, int r
     constexpr int CPL = BN / 64;  // columns per lane: lane + 64 j, coalesced per load
     const float* ob = p.out_f32 + (size_t)nb * p.o_rows * BN + lane;  // this N-block's part of O
     const int c0 = nb * BN + lane;
-    for (int j = wave; j < n; j += NW) {
-        const int t = s_list[j];
-        // lane k < K holds route k's row and weight; the loads of up to 8
-        // routes are issued together, then summed in k order (the block's
-        // tail is latency, not bandwidth: one block per CU)
-        const int kl = lane < K ? lane : 0;
-        const int my_row = p.rt2row[(size_t)t * K + kl];
-        const float my_w = p.on_input ? 1.0f : p.topw[(size_t)t * K + kl];
-        float a[CPL];
+    // two tokens per round when K <= 32 (lanes 32 + k hold the second one's
+    // routes): the block's tail is latency, not bandwidth (one block per CU),
+    // so the loads of up to 8 routes of both tokens are issued together, then
+    // each token is summed in k order
+    const int TB = K <= 32 ? 2 : 1;
+    for (int j = TB * wave; j < n; j += TB * NW) {
+        const bool two = TB == 2 && j + 1 < n;
+        const int t0 = s_list[j], t1 = two ? s_list[j + 1] : t0;
+        const int k = TB == 2 ? (lane & 31) : lane;  // route of this lane
+        const int tl = lane < 32 ? t0 : t1;
+        int my_row = 0;
+        float my_w = 1.0f;
+        if (k < K && (TB == 1 || lane < 32 || two)) {
+            my_row = p.rt2row[(size_t)tl * K + k];
+            if (!p.on_input) my_w = p.topw[(size_t)tl * K + k];
+        }
+        float a0[CPL], a1[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) a[c] = 0.0f;
+        for (int c = 0; c < CPL; ++c) a0[c] = a1[c] = 0.0f;
         for (int k0 = 0; k0 < K; k0 += 8) {
-            float q[8][CPL];
+            float q0[8][CPL], q1[8][CPL];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (k0 + u < K) {
-                    const int row = __builtin_amdgcn_readlane(my_row, k0 + u);
-                    const float* o = ob + (size_t)row * BN;
+                    const float* o = ob + (size_t)__builtin_amdgcn_readlane(my_row, k0 + u) * BN;
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
-                        q[u][c] = __hip_atomic_load(o + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        q0[u][c] = __hip_atomic_load(o + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (two) {
+                        const float* o1 = ob + (size_t)__builtin_amdgcn_readlane(my_row, 32 + k0 + u) * BN;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c)
+                            q1[u][c] = __hip_atomic_load(o1 + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (k0 + u < K) {
-                    const float w = __builtin_bit_cast(
+                    const float w0 = __builtin_bit_cast(
                         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), k0 + u));
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) a[c] = __fmaf_rn(w, q[u][c], a[c]);
+                    for (int c = 0; c < CPL; ++c) a0[c] = __fmaf_rn(w0, q0[u][c], a0[c]);
+                    if (two) {
+                        const float w1 = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), 32 + k0 + u));
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) a1[c] = __fmaf_rn(w1, q1[u][c], a1[c]);
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) p.y[(size_t)t * p.N + c0 + 64 * c] = bf16_rne(a[c]);
+        for (int c = 0; c < CPL; ++c) p.y[(size_t)t0 * p.N + c0 + 64 * c] = bf16_rne(a0[c]);
+        if (two) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) p.y[(size_t)t1 * p.N + c0 + 64 * c] = bf16_rne(a1[c]);
+        }
     }
 }
 

@@ -97,6 +97,20 @@ def test_largest_e_and_k():
     _run_and_check(inp, 64, "w4a4_tensor", True, what="K=64")
 
 
+@pytest.mark.parametrize("K", [12, 33, 64])
+def test_fused_finalize_large_k(K):
+    """The fused finalize with more routes than one read-back batch (K > 8)
+    and with one token per read-back round (K > 32): against the oracle, and
+    bit for bit against the deterministic finalize."""
+    print(f"case fused K={K}", flush=True)
+    inp = Inputs(6, 256, 128, 64, K, "relu2", "normal")
+    _, _, _, y_f, _, _ = run_layer(inp, K, "w4a4_tensor", True, False)
+    _run_and_check(inp, K, "w4a4_tensor", True, det=False, what=f"fused K={K}")
+    _, _, _, y_d, _, _ = run_layer(inp, K, "w4a4_tensor", True, True)
+    torch.cuda.synchronize()
+    assert torch.equal(y_f, y_d), f"K={K}: fused and deterministic outputs differ"
+
+
 def test_ties_in_logits():
     """Exactly equal logits: lower expert ids win; the permutation stays stable."""
     T, E = 48, 16
