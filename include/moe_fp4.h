@@ -20,8 +20,10 @@
  *                or stored as bf16 (W4A16);
  *   S6 FC2       grouped GEMM o = a W2_e^T per route;
  *   S7 finalize  y[t] = sum_k w[t,k] o[route t*K+k] with w = p (output side) or
- *                1 (input side, the weight was applied before FC2), either in
- *                fixed k order (deterministic) or fused into FC2 by atomics.
+ *                1 (input side, the weight was applied before FC2), in fixed k
+ *                order, either as its own kernel (deterministic) or fused into
+ *                FC2 (the FC2 block completing a token's K routes for its
+ *                columns reduces them; the same bits).
  *
  * Conventions for every entry point:
  *  - Tensor pointers are device pointers (hipMalloc'd or equivalent), row-major,
