@@ -443,7 +443,6 @@ int moe::enqueue_forward(const moe_dims* d, const void* prepared, const uint16_t
     g2.out_f32 = WS(float, V_O);
     g2.fused = fused ? FUSE_ARRIVE : FUSE_NONE;
     g2.arrive = WS(uint32_t, V_ARRIVE);
-    g2.o_rows = R;
     g2.rt2row = rt2row;
     g2.y = y;
     g2.status = status;

@@ -76,7 +76,7 @@ __device__ __forceinline__ float row16_max(float v) {
 template <int AB, int MS, int WN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS][WN], int e,
                                               int row0, int rows, const int* s_arow, int gs0,
-                                              int lane, int nb, int bn) {
+                                              int lane) {
     const float gw = p.b_g ? p.b_g[e] : 1.0f;
     const int c16 = lane & 15;
     if constexpr (EPI == EPI_FC1 && AB == AB_FP8) {
@@ -168,9 +168,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x4 (&acc)[MS
                 }
             } else {
                 if (p.fused == FUSE_ARRIVE) {
-                    // N-block-major O, with device scope: rows are read back by
-                    // a block on any XCD
-                    float* o = p.out_f32 + ((size_t)nb * p.o_rows + row) * bn + (gs0 * 16 - nb * bn) + c16;
+                    // device scope: rows are read back by a block on any XCD
+                    float* o = p.out_f32 + (size_t)row * p.N + gs0 * 16 + c16;
 #pragma unroll
                     for (int s = 0; s < WN; ++s)
                         __hip_atomic_store(o + s * 16, acc[ms][s][i] * sc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -245,12 +244,9 @@ __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "m
 // finalize's arithmetic in its order, so both variants give the same bits, and
 // no fp32 atomics touch the output: a token's columns are written once, by
 // whichever block arrives last.
-// O is stored N-block-major ([N / BN][R][BN]) in this mode, so that the rows
-// of one N-block form one contiguous region. The wide tiles' block order
-// gives each XCD a contiguous range of (N-block, M-tile) pairs, so the blocks
-// of an N-block, hence the writers and the reader of a token's rows for it,
-// mostly share one L2 (an N-block-major order over the whole chip ran this
-// FC2 1.5x slower at 16k tokens: 5.57 against 3.79 ms).
+// The wide tiles keep their block order, which gives each XCD a contiguous
+// range of (N-block, M-tile) pairs: an N-block-major order over the whole
+// chip ran this FC2 1.5x slower at 16k tokens (5.57 against 3.79 ms).
 // Visibility across XCDs (each has its own L2) uses device-scope accesses on
 // the O rows themselves rather than device-scope fences, which write back or
 // invalidate a whole L2 (measured: 3x slower FC2 at 16k tokens, 9x on the
@@ -275,12 +271,12 @@ __device__ __forceinline__ void arrive_finalize(const GemmArgs& p, int nb, int r
     __syncthreads();
     const int n = *s_n;
     constexpr int CPL = BN / 64;  // columns per lane: lane + 64 j, coalesced per load
-    const float* ob = p.out_f32 + (size_t)nb * p.o_rows * BN + lane;  // this N-block's part of O
+    const float* ob = p.out_f32 + (size_t)nb * BN + lane;  // this N-block's columns of O
     const int c0 = nb * BN + lane;
     // two tokens per round when K <= 32 (lanes 32 + k hold the second one's
-    // routes): the block's tail is latency, not bandwidth (one block per CU),
-    // so the loads of up to 8 routes of both tokens are issued together, then
-    // each token is summed in k order
+    // routes): the loads of up to 8 routes of both tokens are issued
+    // together, then each token is summed in k order (on the decode tiles,
+    // whose blocks all run at once, this tail is latency)
     const int TB = K <= 32 ? 2 : 1;
     for (int j = TB * wave; j < n; j += TB * NW) {
         const bool two = TB == 2 && j + 1 < n;
@@ -301,12 +297,12 @@ __device__ __forceinline__ void arrive_finalize(const GemmArgs& p, int nb, int r
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 if (k0 + u < K) {
-                    const float* o = ob + (size_t)__builtin_amdgcn_readlane(my_row, k0 + u) * BN;
+                    const float* o = ob + (size_t)__builtin_amdgcn_readlane(my_row, k0 + u) * p.N;
 #pragma unroll
                     for (int c = 0; c < CPL; ++c)
                         q0[u][c] = __hip_atomic_load(o + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (two) {
-                        const float* o1 = ob + (size_t)__builtin_amdgcn_readlane(my_row, 32 + k0 + u) * BN;
+                        const float* o1 = ob + (size_t)__builtin_amdgcn_readlane(my_row, 32 + k0 + u) * p.N;
 #pragma unroll
                         for (int c = 0; c < CPL; ++c)
                             q1[u][c] = __hip_atomic_load(o1 + 64 * c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -701,7 +697,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GemmArgs p) {
         for (int u = 0; u < P - 1; ++u)
             if (kt0 + u < KT) step(kt0 + u, u);
         wait_vmcnt<0>();
-        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane, nb, 16 * NW * WN);
+        gemm_epilogue<AB, MS, WN, EPI>(p, acc, e, row0, rows, s_arow, gs0, lane);
     };
     if constexpr (BM >= 64) {
         if (rows > BM / 2) body(std::integral_constant<int, BM / 16>{});

@@ -100,9 +100,7 @@ struct GemmArgs {
     uint8_t* a2_scales;  //            and their E8M0 block scales [R][I/32]
     uint32_t* amax_slot; // FC1: kAmaxSlots partial maxima of the FC2 input, kAmaxStride apart (NVFP4 per-tensor)
     int fused;           // FC2: FUSE_NONE or FUSE_ARRIVE
-    uint32_t* arrive;    // FC2 fused by arrival counts: [T][N / block columns] counters, zero on entry;
-                         //   O is then N-block-major, [N / BN][R][BN] for block columns BN
-    int o_rows;          //   R, the rows of O
+    uint32_t* arrive;    // FC2 fused by arrival counts: [T][N / block columns] counters, zero on entry
     const int32_t* rt2row;  //   route (t, k) -> its row of O
     uint16_t* y;         //   bf16 output [T][N]
     const uint32_t* status;  // the forward's status word: blocks exit when it is not 0

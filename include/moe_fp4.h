@@ -201,8 +201,7 @@ int moe_quantize(const float* v, int32_t rows, int32_t cols, int32_t kind, uint8
  *   6 x codes                    7 x scales               8 x global scale(s) f32
  *   9 FC2 input, fp32 before quantization [R][I] (W4A4) or bf16 (W4A16)
  *   10 FC2-input codes           11 FC2-input scales      12 FC2-input global scale(s)
- *   13 permuted FC2 output O [R][H] f32 (deterministic finalize; after a
- *      fused forward the view holds O in a column-blocked order)
+ *   13 permuted FC2 output O [R][H] f32 (either finalize)
  *   14/15 x re-blocked to MXFP4: codes [T][H/2], E8M0 scales [T][H/32] (mode 5)
  *   16/17 FC2 input re-blocked to MXFP4: codes [R][I/2], scales [R][I/32] (mode 5)
  * Returns MOE_ERR_INVALID for a view the mode does not produce. */
