@@ -210,8 +210,11 @@ def roofline(wl, d, counts, st_us, decode):
     return r
 
 
-def run_workload(name, args, with_cpu):
-    """Times one workload (both finalize variants it runs); returns its record."""
+def run_workload(name, args, with_cpu, min_timed_s=0.0):
+    """Times one workload (both finalize variants it runs); returns its record.
+    min_timed_s > 0 (sub-records): the graph replays are repeated until they
+    span at least that long, so that host jitter does not dominate the mean of
+    a layer that takes tens of microseconds."""
     import numpy as np
     import torch
 
@@ -282,8 +285,16 @@ def run_workload(name, args, with_cpu):
         for i in range(args.warmup):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
+        nrep = args.steps
+        if min_timed_s > 0:  # a first estimate of the step time sets the count
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                graphs[i % copies].replay()
+            torch.cuda.synchronize()
+            est = (time.perf_counter() - t0) / args.steps
+            nrep = max(args.steps, min(5000, int(min_timed_s / max(est, 1e-6)) + 1))
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(nrep):
             graphs[i % copies].replay()
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
@@ -297,7 +308,7 @@ def run_workload(name, args, with_cpu):
         per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
         pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 5)
                for q in (10, 50, 90)}
-        variants[fin] = {"ms": dt / args.steps * 1e3, "pct": pct,
+        variants[fin] = {"ms": dt / nrep * 1e3, "pct": pct, "replays": nrep,
                          "st_us": {k: v / max(nfw, 1) * 1e3 for k, v in st.items()}}
         del graphs
 
@@ -318,6 +329,7 @@ def run_workload(name, args, with_cpu):
                    "timing": "hipGraph replay of one forward per step",
                    "weight_copies_rotated": copies, "touched_experts": touched,
                    "routing": routing_summary(counts)},
+        "graph_replays_timed": v["replays"],
         "graph_step_ms_percentiles": v["pct"],
         "stages_us": {k: round(u, 2) for k, u in v["st_us"].items()},
         "layer_tflops": round(flops / (v["ms"] * 1e-3) / 1e12, 2),
@@ -328,6 +340,7 @@ def run_workload(name, args, with_cpu):
         o = variants[other]
         rec["deterministic_finalize" if other == "det" else "fused_finalize"] = {
             "value": round(wl.T / (o["ms"] * 1e-3), 1), "ms_per_step": round(o["ms"], 5),
+            "graph_replays_timed": o["replays"],
             "graph_step_ms_percentiles": o["pct"],
             "stages_us": {k: round(u, 2) for k, u in o["st_us"].items()},
             "roofline": roofline(wl, d, counts, o["st_us"], decode)}
@@ -365,7 +378,7 @@ def main():
             if name == args.workload:
                 continue
             print(f"# sub-record {name}", file=sys.stderr, flush=True)
-            out["workloads"][name] = run_workload(name, args, False)
+            out["workloads"][name] = run_workload(name, args, False, min_timed_s=0.1)
     print(json.dumps(out))
 
 
