@@ -100,6 +100,25 @@ def test_random_shape(case):
     check_layer(moe, d, ws, y, ref, W, T, K, mode, on_input, what, round_allow=True)
 
 
+@pytest.mark.parametrize("case", _cases() + _big_cases() + _route_cases(), ids=lambda c: f"case{c[0]}")
+def test_fused_equals_deterministic(case):
+    """On every sampled shape and mode, the fused finalize (the FC2 block
+    completing a token's routes reduces them) gives the deterministic
+    finalize's bits: the arrival counts on every tile configuration (16- to
+    128-row tiles, two or four strips per wave, four or eight waves)."""
+    i, T, H, I, E, K, act, mode, on_input, _, logits = case
+    what = f"case{i} T={T} H={H} I={I} E={E} K={K} {act} {mode} on_input={on_input} {logits}"
+    print(what, flush=True)
+    inp = Inputs(T, H, I, E, K, act, logits, seed=100 + i)
+    d = moe.Dims(E, H, I, act, R.weight_format(mode))
+    blob = moe.prepare_weights(d, inp.w1, inp.w2)
+    y_d = moe.forward(d, blob, inp.x, inp.logits, K, mode, on_input, True)
+    y_f = moe.forward(d, blob, inp.x, inp.logits, K, mode, on_input, False)
+    torch.cuda.synchronize()
+    ndiff = int((y_f.view(torch.int16) != y_d.view(torch.int16)).sum().item())
+    assert ndiff == 0, f"{what}: fused and deterministic outputs differ in {ndiff} elements"
+
+
 @pytest.mark.parametrize("mode", MODES)
 def test_workspace_reuse_across_shapes(mode):
     """A workspace sized for a large batch, reused for a smaller one right after:
