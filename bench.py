@@ -59,8 +59,8 @@ CPU_SAMPLE_TOKENS = {"tiny_w4a4_tensor_T16_H256_I128_E8_K2": 16,
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-subrecords", action="store_true",
                     help="time the headline workload only")
